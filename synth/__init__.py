@@ -1,0 +1,7 @@
+"""Seeded synthetic inputs for block-sparse FP8 attention prefill.
+
+This package only draws random data and lays it out (quantised Q/K/V, paged
+caches, page tables, block masks).  It holds none of the attention arithmetic,
+and both the oracle-side tests and the GPU-side tests/benchmark use it.
+"""
+from .workloads import CONFIGS, Problem, make_problem, WorkloadConfig  # noqa: F401
