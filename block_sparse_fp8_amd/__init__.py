@@ -1,0 +1,191 @@
+"""Block-sparse FP8 (E4M3) attention prefill over a paged KV cache, MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in ``include/bsa_fp8.h``: it
+checks tensor devices/dtypes, allocates outputs with torch, passes raw device
+pointers and torch's current stream, and raises on a non-zero status.  Every
+step of the computation runs in the HIP library ``libbsa_fp8.so``; there is no
+other code path.  If the library has not been built, importing this package
+still works but every call raises ``RuntimeError``.
+"""
+import ctypes
+import enum
+import math
+import os
+
+import torch
+
+__all__ = [
+    "QuantType",
+    "KVLayout",
+    "BsaError",
+    "bsa_fp8_prefill",
+    "attention_with_kvcache_blocksparse_prefill_fp8",
+    "library_path",
+    "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libbsa_fp8.so"
+
+
+def library_path():
+    return os.path.join(_HERE, LIB_NAME)
+
+
+class QuantType(enum.IntEnum):
+    """Quantisation schemes (hpc-ops article, "FP8 Tensor Core compute")."""
+    QPERTOKEN_PERHEAD_KPERTENSOR_VPERTENSOR = 0
+    QPERTOKEN_PERHEAD_KPERTOKEN_PERHEAD_VPERHEAD = 1
+
+
+class KVLayout(enum.IntEnum):
+    NHD = 0  # [num_pages, page_size, Hkv, 128]
+    HND = 1  # [num_pages, Hkv, page_size, 128]
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"bsa_fp8_prefill failed (status {status}): {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("num_heads_q", ctypes.c_int32),
+        ("num_heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("mask_tiles_q", ctypes.c_int32),
+        ("mask_tiles_kv", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+_lib_handle = None
+
+
+def load_library():
+    """Load libbsa_fp8.so (once).  Raises RuntimeError if it is not built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m block_sparse_fp8_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.bsa_fp8_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_int, ctypes.c_int, ctypes.POINTER(Dims), vp, vp, vp]
+    lib.bsa_fp8_prefill.restype = ctypes.c_int
+    lib.bsa_fp8_status_string.argtypes = [ctypes.c_int]
+    lib.bsa_fp8_status_string.restype = ctypes.c_char_p
+    lib.bsa_fp8_abi_version.argtypes = []
+    lib.bsa_fp8_abi_version.restype = ctypes.c_int
+    _lib_handle = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().bsa_fp8_status_string(int(status)).decode()
+
+
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, dtypes, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def bsa_fp8_prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
+                    seqlens_kv, block_mask, quant_type, page_size, *, max_seqlen_q,
+                    kv_layout=KVLayout.NHD, causal=True, softmax_scale=None,
+                    out=None, lse=None, return_lse=True, stream=None):
+    """Call the C entry point of the same name.  Returns (out, lse).
+
+    Shapes and meaning are those of ``include/bsa_fp8.h``.  ``out`` (bf16
+    [T,Hq,128]) and ``lse`` (float32 [Hq,T]) are allocated when not given.
+    """
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("bsa_fp8_prefill runs on a GPU; q is on " + str(device))
+    _check("q", q, _FP8, device)
+    _check("kcache", kcache, _FP8, device)
+    _check("vcache", vcache, _FP8, device)
+    for name, t in (("qscale", qscale), ("kscale", kscale), ("vscale", vscale)):
+        _check(name, t, (torch.float32,), device)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("block_table", block_table),
+                    ("seqlens_kv", seqlens_kv)):
+        _check(name, t, (torch.int32,), device)
+    if block_mask is not None:
+        _check("block_mask", block_mask, (torch.uint8, torch.bool), device)
+        if block_mask.dim() != 4:
+            raise ValueError("block_mask must be [B, Hq, mask_tiles_q, mask_tiles_kv]")
+    if q.dim() != 3 or kcache.dim() != 4 or vcache.shape != kcache.shape:
+        raise ValueError("q must be [T,Hq,D]; kcache/vcache must be 4-D and of equal shape")
+    T, Hq, D = q.shape
+    kv_layout = KVLayout(int(kv_layout))
+    Hkv = kcache.shape[2] if kv_layout == KVLayout.NHD else kcache.shape[1]
+    B = seqlens_kv.shape[0]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=device)
+    else:
+        _check("out", out, (torch.bfloat16,), device)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=device)
+    elif lse is not None:
+        _check("lse", lse, (torch.float32,), device)
+    dims = Dims(batch=B, total_q=T, num_heads_q=Hq, num_heads_kv=Hkv, head_dim=D,
+                num_pages=kcache.shape[0], max_pages_per_seq=block_table.shape[1],
+                max_seqlen_q=int(max_seqlen_q),
+                mask_tiles_q=block_mask.shape[2] if block_mask is not None else 0,
+                mask_tiles_kv=block_mask.shape[3] if block_mask is not None else 0,
+                kv_layout=int(kv_layout), causal=1 if causal else 0,
+                softmax_scale=float(softmax_scale))
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    lib = load_library()
+    mask_u8 = block_mask.view(torch.uint8) if block_mask is not None else None
+    status = lib.bsa_fp8_prefill(
+        _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(qscale), _ptr(kscale), _ptr(vscale),
+        _ptr(cu_seqlens_q), _ptr(block_table), _ptr(seqlens_kv), _ptr(mask_u8),
+        int(quant_type), int(page_size), ctypes.byref(dims), _ptr(out), _ptr(lse),
+        ctypes.c_void_p(stream))
+    if status != 0:
+        raise BsaError(status, status_string(status))
+    return out, lse
+
+
+def attention_with_kvcache_blocksparse_prefill_fp8(
+        q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_ids, seqlens_kvcache,
+        max_seqlens_q, quant_type=QuantType.QPERTOKEN_PERHEAD_KPERTENSOR_VPERTENSOR,
+        block_mask=None, kv_layout="NHD", softmax_scale=None, causal=True):
+    """The call shape of the hpc-ops quick-start example (hpc-ops article,
+    "Quick start"): page size comes from the cache shape, the layout is named
+    by string, and the result is (out, lse)."""
+    layout = KVLayout[kv_layout] if isinstance(kv_layout, str) else KVLayout(int(kv_layout))
+    page_size = kcache.shape[1] if layout == KVLayout.NHD else kcache.shape[2]
+    return bsa_fp8_prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_ids,
+                           seqlens_kvcache, block_mask, int(quant_type), page_size,
+                           max_seqlen_q=max_seqlens_q, kv_layout=layout, causal=causal,
+                           softmax_scale=softmax_scale)

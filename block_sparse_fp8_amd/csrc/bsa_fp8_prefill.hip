@@ -1,0 +1,550 @@
+// Block-sparse FP8 (E4M3) attention prefill over a paged KV cache, gfx950.
+//
+// One workgroup of 256 threads (4 waves) owns one (sequence, q-head, 128-query
+// tile); wave w owns queries 32w..32w+31.  Two workgroups share a CU so that
+// one's softmax (VALU) overlaps the other's matrix products.
+//
+//   1. Active-tile compaction (hpc-ops article, "Active tile list"): each wave
+//      ballots the Q tile's uint8 mask row 64 KV tiles at a time and walks the
+//      set bits in ascending order, so every wave sees the same ordered list
+//      without a round trip through LDS.  The candidates are clipped to the KV
+//      length and, in causal mode, to the last tile any query of the Q tile can
+//      see.  Tiles the mask switches off are never read.
+//   2. Per active tile, K and V rows are gathered from the paged cache (one
+//      page-table lookup per row).  V (and, for per-token K scales, the K
+//      descales) go straight to LDS with direct-to-LDS loads, double-buffered;
+//      K goes through registers, one tile ahead.
+//   3. S^T = K . Q^T.  E4M3 -> f16 is exact (a bit shift that scales values by
+//      2^-8), so K is widened to f16 once per workgroup when it is staged in
+//      LDS and Q once in registers, and the product runs on
+//      v_mfma_f32_32x32x16_f16, whose accumulation is fp32-accurate.  (The
+//      E4M3 matrix path keeps only about 14 bits below the largest product of
+//      a dot product, which moves P across E4M3 rounding boundaries.)
+//      Computing S^T makes every lane own one query, so the running max, sum
+//      and rescale are per lane.  K rows are read in a permuted order so that
+//      the accumulator registers of lane half h hold keys h*32..h*32+31 of each
+//      64-key half of the tile, in register order.
+//   4. Online softmax in fp32 in the log2 domain: qscale*softmax_scale*log2(e)
+//      (and the per-tensor K descale, and 2^16 for the f16 widening) is one
+//      per-lane constant; P' = exp2(x - m + 8) = 256*exp(score - max), i.e. the
+//      fixed P-scale of 256 (hpc-ops article, "FP8 Tensor Core compute: fixed
+//      P-scale quantisation") costs nothing.  P' is rounded to E4M3
+//      (v_cvt_pk_fp8_f32, round to nearest even) and the row sum keeps the
+//      unrounded P'.  The accumulator rescale is skipped when no row of the
+//      wave has a new maximum (the factor is then exactly 1).
+//   5. O^T += V^T . P^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3).  V stays
+//      row-major in LDS; the transposing read ds_read_b64_tr_b8 delivers it
+//      key-major.
+//   6. Epilogue: O = O_acc * vdescale / sum(P') (the 1/256 is inside the sum),
+//      written as bf16; LSE = ln2 * (m + log2(sum) - 8).  A query whose sparse
+//      set is empty gets O = 0 and LSE = -FLT_MAX ("Quant Block Sparse
+//      Attention", "Sparse indices & PA page table").
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "bsa_fp8.h"
+
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kHeadDim = 128;
+constexpr int kThreads = 256;
+constexpr int kK16Row = 2 * kHeadDim;  // bytes per f16 K row in LDS
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kPScaleLog2 = 8.0f;      // P is scaled by 2^8 = 256 before rounding to E4M3
+constexpr float kF16Widen = 65536.0f;    // undoes the 2^-8 of the f16 widening of Q and of K
+constexpr float kNegFltMax = -3.402823466e+38f;
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+struct Params {
+  const uint8_t* q;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const float* qscale;
+  const float* kscale;
+  const float* vscale;
+  const int32_t* cu_q;
+  const int32_t* block_table;
+  const int32_t* seqlens_kv;
+  const uint8_t* mask;
+  uint16_t* out;
+  float* lse;
+  int B, T, Hq, Hkv, group;
+  int page_size, page_shift, max_pages;
+  int mt, mkv, mt_grid;
+  int layout, causal;
+  float qk_scale;  // softmax_scale * log2(e) * 2^16
+};
+
+// 16-byte chunk swizzle of the fp8 V rows (128 B, 8 chunks) in LDS.
+__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ (((row >> 5) & 1) << 2); }
+
+__device__ __forceinline__ int64_t kv_row_index(const Params& p, int page, int slot, int g) {
+  return p.layout == BSA_KV_NHD ? ((int64_t)page * p.page_size + slot) * p.Hkv + g
+                                : ((int64_t)page * p.Hkv + g) * p.page_size + slot;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Four E4M3 codes (one dword) -> four f16 values holding code_value * 2^-8,
+// exactly (E4M3 subnormals land on f16 subnormals).  Returned as two dwords.
+__device__ __forceinline__ v2i e4m3x4_to_f16x4(uint32_t w) {
+  // place codes in the high byte of each 16-bit half: [0,c0,0,c1] and [0,c2,0,c3]
+  const uint32_t lo = __builtin_amdgcn_perm(0u, w, 0x010c000cu);
+  const uint32_t hi = __builtin_amdgcn_perm(0u, w, 0x030c020cu);
+  const uint32_t flo = (lo & 0x80008000u) | ((lo >> 1) & 0x3f803f80u);
+  const uint32_t fhi = (hi & 0x80008000u) | ((hi >> 1) & 0x3f803f80u);
+  return v2i{(int)flo, (int)fhi};
+}
+
+__device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
+  // E4M3 (format 0) for both operands, no block scales.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// Wave-uniform walk over the active KV tiles of one Q tile, in ascending order.
+struct TileWalk {
+  const uint8_t* row;  // mask row, or nullptr for the dense path
+  int n_end;           // candidates are 0 .. n_end-1
+  int base;            // first candidate of the current 64-tile chunk
+  uint64_t bits;       // active candidates of the chunk not yet returned
+
+  __device__ void init(const uint8_t* r, int end, int lane) {
+    row = r;
+    n_end = end;
+    base = 0;
+    bits = load_chunk(lane);
+  }
+  __device__ uint64_t load_chunk(int lane) const {
+    const int n = base + lane;
+    const bool act = n < n_end && (row == nullptr || row[n] != 0);
+    return __ballot(act);
+  }
+  // Next active tile, or -1.
+  __device__ int next(int lane) {
+    while (bits == 0) {
+      base += 64;
+      if (base >= n_end) return -1;
+      bits = load_chunk(lane);
+    }
+    const int n = base + (int)__builtin_ctzll(bits);
+    bits &= bits - 1;
+    return n;
+  }
+};
+
+template <int QUANT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bsa_fp8_prefill_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) uint8_t k16_lds[kTile * kK16Row];       // 32 KB
+  __shared__ __attribute__((aligned(16))) uint8_t v8_lds[2][kTile * kHeadDim];    // 32 KB
+  __shared__ __attribute__((aligned(16))) float ks_lds[2][kTile];                 // 1 KB
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hd = lane >> 5;   // lane half
+  const int col = lane & 31;  // query column owned by this lane within the wave
+
+  // Heavy-first order: the largest Q-tile index (most causal work) first.
+  const int per_m = p.B * p.Hq;
+  const int m = p.mt_grid - 1 - (int)(blockIdx.x / per_m);
+  const int rem = (int)(blockIdx.x % per_m);
+  const int b = rem / p.Hq;
+  const int h = rem % p.Hq;
+  const int g = h / p.group;
+
+  const int t0 = p.cu_q[b];
+  const int lq = p.cu_q[b + 1] - t0;
+  const int lkv = p.seqlens_kv[b];
+  if (m * kTile >= lq) return;  // Q tile beyond this sequence (uniform per workgroup)
+
+  // Candidate KV tiles: below the KV length, within the causal range of some
+  // query of this Q tile, and within the mask width.
+  int n_end = (lkv + kTile - 1) / kTile;
+  if (p.causal) {
+    const int p_max = lkv - lq + min(m * kTile + kTile - 1, lq - 1);
+    n_end = p_max >= 0 ? min(n_end, p_max / kTile + 1) : 0;
+  }
+  const uint8_t* mask_row = nullptr;
+  if (p.mask != nullptr) {
+    n_end = min(n_end, p.mkv);
+    mask_row = p.mask + (((int64_t)b * p.Hq + h) * p.mt + m) * p.mkv;
+  }
+  TileWalk walk;
+  walk.init(mask_row, n_end, lane);
+
+  // Queries of this lane.
+  const int tq = m * kTile + wave * 32 + col;             // query index within the sequence
+  const bool q_valid = tq < lq;
+  const int p_pos = lkv - lq + tq;                        // causal position of this query
+  const int p_wave_min = lkv - lq + m * kTile + wave * 32;  // smallest position in the wave
+
+  // Q operand (B of S^T = K.Q^T, f16 32x32x16): lane holds query `col`,
+  // head-dim elements ks*16 + hd*8 .. +7 for ks = 0..7.
+  v8h qh[8];
+  float cscale = 0.0f;
+  {
+    v2i raw[8];
+    if (q_valid) {
+      const uint8_t* qp = p.q + ((int64_t)(t0 + tq) * p.Hq + h) * kHeadDim + hd * 8;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) raw[ks] = *reinterpret_cast<const v2i*>(qp + ks * 16);
+      cscale = p.qscale[(int64_t)(t0 + tq) * p.Hq + h] * p.qk_scale;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) raw[ks] = v2i{0, 0};
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const v2i a = e4m3x4_to_f16x4((uint32_t)raw[ks][0]);
+      const v2i c = e4m3x4_to_f16x4((uint32_t)raw[ks][1]);
+      const v4i w = v4i{a[0], a[1], c[0], c[1]};
+      qh[ks] = __builtin_bit_cast(v8h, w);
+    }
+  }
+  if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR) cscale *= p.kscale[0];
+  const float vdesc = QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR ? p.vscale[0] : p.vscale[g];
+
+  v16f oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.0f;
+  float m_run = -INFINITY;  // running max of x = score * log2(e)
+  float l_run = 0.0f;       // this lane's half of sum(P'), P' = 2^(x - m + 8)
+
+  // K operand rows: accumulator row i of block c holds key
+  // (c>>1)*64 + hi*32 + (c&1)*16 + ri with hi = (i>>2)&1, ri = (i>>3)*4 + (i&3).
+  const int hi_a = (col >> 2) & 1;
+  const int ri_a = ((col >> 3) << 2) | (col & 3);
+
+  // Staging roles: K through registers, one row per thread (row tid & 127,
+  // head-dim bytes 64*(tid>>7) .. +63); V by direct-to-LDS loads (wave w: rows
+  // 32w..32w+31, 8 rows of 128 bytes per instruction).
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+  const int krow_ld = tid & (kTile - 1);
+  const int khalf = tid >> 7;
+  v4i kreg[4];
+
+  auto issue_tile = [&](int n, int buf) {
+    {
+      const int j = n * kTile + krow_ld;
+      if (j < lkv) {
+        const int64_t r = kv_row_index(p, bt[j >> p.page_shift], j & (p.page_size - 1), g);
+        const v4i* src = reinterpret_cast<const v4i*>(p.kc + r * kHeadDim + khalf * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kreg[i] = src[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kreg[i] = v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave * 32 + i * 8 + (lane >> 3);
+      const int pchunk = lane & 7;
+      int j = n * kTile + row;
+      if (j >= lkv) j = n * kTile;  // rows past the KV length read a valid row; P is 0 there
+      const int64_t r = kv_row_index(p, bt[j >> p.page_shift], j & (p.page_size - 1), g);
+      const uint8_t* src = p.vc + r * kHeadDim + ((pchunk ^ swz8(row)) << 4);
+      __builtin_amdgcn_global_load_lds((glb_void*)src,
+                                       (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
+    }
+    if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD && wave < 2) {
+      int j = n * kTile + wave * 64 + lane;
+      if (j >= lkv) j = n * kTile;
+      const int64_t r = kv_row_index(p, bt[j >> p.page_shift], j & (p.page_size - 1), g);
+      __builtin_amdgcn_global_load_lds((glb_void*)(p.kscale + r), (lds_void*)(&ks_lds[buf][wave * 64]), 4, 0, 0);
+    }
+  };
+
+  int n = walk.next(lane);
+  int buf = 0;
+  if (n >= 0) issue_tile(n, 0);
+
+  while (n >= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // k16 and the other V buffer are no longer read; this tile's V is in LDS
+    // Widen this tile's K to f16 in LDS.  Layout is chunk-major: the 16-byte
+    // chunk c (head-dim elements 8c..8c+7) of key row r sits at c*2048 + r*16.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v2i a = e4m3x4_to_f16x4((uint32_t)kreg[i][0]);
+      const v2i c = e4m3x4_to_f16x4((uint32_t)kreg[i][1]);
+      const v2i d = e4m3x4_to_f16x4((uint32_t)kreg[i][2]);
+      const v2i e = e4m3x4_to_f16x4((uint32_t)kreg[i][3]);
+      const int chunk = 8 * khalf + 2 * i;
+      *reinterpret_cast<v4i*>(k16_lds + chunk * 2048 + krow_ld * 16) = v4i{a[0], a[1], c[0], c[1]};
+      *reinterpret_cast<v4i*>(k16_lds + (chunk + 1) * 2048 + krow_ld * 16) = v4i{d[0], d[1], e[0], e[1]};
+    }
+    __syncthreads();  // k16 ready
+    const int n_next = walk.next(lane);
+    if (n_next >= 0) issue_tile(n_next, buf ^ 1);
+
+    // ---- S^T = K . Q^T (f16 operands, fp32 accumulation) ------------------
+    v16f s[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int krow = (c >> 1) * 64 + hi_a * 32 + (c & 1) * 16 + ri_a;
+      const uint8_t* kp = k16_lds + hd * 2048 + krow * 16;
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const v8h a = *reinterpret_cast<const v8h*>(kp + ks * 4096);
+        acc = mfma_f16(a, qh[ks], acc);
+      }
+      s[c] = acc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Lane holds, for its query, keys key(c, r) = (c>>1)*64 + hd*32 + (c&1)*16 + r.
+    if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float* ksp = &ks_lds[buf][(c >> 1) * 64 + hd * 32 + (c & 1) * 16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[c][r] *= ksp[r];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const bool band = (p.causal && n * kTile + kTile - 1 > p_wave_min) || (n * kTile + kTile > lkv);
+    if (band) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = n * kTile + (c >> 1) * 64 + hd * 32 + (c & 1) * 16 + r;
+          const bool ok = j < lkv && (!p.causal || j <= p_pos);
+          s[c][r] = ok ? s[c][r] : -INFINITY;
+        }
+    }
+
+    // ---- online softmax ------------------------------------------------------
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) tmax = max3f(tmax, s[c][r], s[c][r + 1]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float tmax_x = tmax == -INFINITY ? -INFINITY : tmax * cscale;
+    const float m_new = fmaxf(m_run, tmax_x);
+    const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);  // exp2(-inf) = 0
+    const float bias = kPScaleLog2 - m_safe;
+    const bool rescale = __ballot(m_new != m_run) != 0;
+    m_run = m_new;
+
+    v8i pk[2];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        float e0 = __builtin_amdgcn_exp2f(fmaf(s[c][r], cscale, bias));
+        float e1 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 1], cscale, bias));
+        float e2 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 2], cscale, bias));
+        float e3 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 3], cscale, bias));
+        if (band) {
+          e0 = s[c][r] == -INFINITY ? 0.0f : e0;
+          e1 = s[c][r + 1] == -INFINITY ? 0.0f : e1;
+          e2 = s[c][r + 2] == -INFINITY ? 0.0f : e2;
+          e3 = s[c][r + 3] == -INFINITY ? 0.0f : e3;
+        }
+        lsum += (e0 + e1) + (e2 + e3);
+        // bytes (c&1)*16 + r .. +3 of the P operand of PV step c>>1
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+        pk[c >> 1][(c & 1) * 4 + (r >> 2)] = w;
+      }
+    }
+    if (rescale) {
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+    }
+    l_run += lsum;
+
+    // ---- O^T += V^T . P^T ----------------------------------------------------
+    // Transposing read: in each 16-lane group, source lane 2k+q addresses key
+    // row (step*64 + half*32 + 8*rr + k) at head-dim column base + 8q; result
+    // lane i then holds column base + i for those 8 keys.
+    const int grp = lane >> 4;
+    const int il = lane & 15;
+    const int kk = il >> 1;
+    const int qq = il & 1;
+    const int half = grp >> 1;
+    const uint8_t* vbase = v8_lds[buf];
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int chunk = 2 * d + (grp & 1);
+        v8i a;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int vrow = sp * 64 + half * 32 + 8 * rr + kk;
+          const int off = vrow * kHeadDim + ((chunk ^ swz8(vrow)) << 4) + 8 * qq;
+          const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vbase + off));
+          a[2 * rr] = t[0];
+          a[2 * rr + 1] = t[1];
+        }
+        oacc[d] = mfma_f8(a, pk[sp], oacc[d]);
+      }
+    }
+    n = n_next;
+    buf ^= 1;
+  }
+
+  // ---- epilogue ------------------------------------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_valid) return;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv = empty ? 0.0f : vdesc / l_tot;
+  uint16_t* op = p.out + ((int64_t)(t0 + tq) * p.Hq + h) * kHeadDim;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = d * 32 + 8 * r4 + 4 * hd;
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[d][4 * r4 + 0] * inv) |
+                          ((uint32_t)f32_to_bf16_rne(oacc[d][4 * r4 + 1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[d][4 * r4 + 2] * inv) |
+                          ((uint32_t)f32_to_bf16_rne(oacc[d][4 * r4 + 3] * inv) << 16);
+      *reinterpret_cast<v2i*>(op + d0) = v2i{(int)w0, (int)w1};
+    }
+  }
+  if (p.lse != nullptr && hd == 0) {
+    p.lse[(int64_t)h * p.T + t0 + tq] = empty ? kNegFltMax : (m_run + log2f(l_tot) - kPScaleLog2) * kLn2;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsa_fp8_abi_version(void) { return 1; }
+
+const char* bsa_fp8_status_string(int status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case BSA_ERR_HEAD_DIM: return "head_dim must be 128";
+    case BSA_ERR_PAGE_SIZE: return "page_size must be 32 or 64";
+    case BSA_ERR_GQA: return "num_heads_q must be a multiple of num_heads_kv with ratio 1..16";
+    case BSA_ERR_QUANT_TYPE: return "unknown quant_type";
+    case BSA_ERR_KV_LAYOUT: return "unknown kv_layout";
+    case BSA_ERR_SIZE: return "a size is negative or inconsistent";
+    case BSA_ERR_MASK_SHAPE: return "block_mask shape does not cover max_seqlen_q";
+    case BSA_ERR_SOFTMAX_SCALE: return "softmax_scale must be finite";
+    case BSA_ERR_TOO_LARGE: return "problem exceeds a supported limit";
+    case BSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache, const float* qscale,
+                    const float* kscale, const float* vscale, const int32_t* cu_seqlens_q,
+                    const int32_t* block_table, const int32_t* seqlens_kv, const uint8_t* block_mask,
+                    int quant_type, int page_size, const bsa_fp8_dims* dims, void* out, float* lse,
+                    void* stream) {
+  // ---- static validation (host only, before any HIP call) ----
+  if (dims == nullptr) return BSA_ERR_NULL_POINTER;
+  const bsa_fp8_dims d = *dims;
+  if (d.head_dim != kHeadDim) return BSA_ERR_HEAD_DIM;
+  if (page_size != 32 && page_size != 64) return BSA_ERR_PAGE_SIZE;
+  if (quant_type != BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR &&
+      quant_type != BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD)
+    return BSA_ERR_QUANT_TYPE;
+  if (d.kv_layout != BSA_KV_NHD && d.kv_layout != BSA_KV_HND) return BSA_ERR_KV_LAYOUT;
+  if (d.batch < 0 || d.total_q < 0 || d.num_pages < 0 || d.max_pages_per_seq < 0 ||
+      d.max_seqlen_q < 0 || d.num_heads_q <= 0 || d.num_heads_kv <= 0)
+    return BSA_ERR_SIZE;
+  if (d.num_heads_q % d.num_heads_kv != 0) return BSA_ERR_GQA;
+  const int group = d.num_heads_q / d.num_heads_kv;
+  if (group < 1 || group > 16) return BSA_ERR_GQA;
+  if (!(d.softmax_scale == d.softmax_scale) || d.softmax_scale == INFINITY ||
+      d.softmax_scale == -INFINITY)
+    return BSA_ERR_SOFTMAX_SCALE;
+  if (d.causal != 0 && d.causal != 1) return BSA_ERR_SIZE;
+  const int mt_grid = (d.max_seqlen_q + kTile - 1) / kTile;
+  if (block_mask != nullptr) {
+    if (d.mask_tiles_q <= 0 || d.mask_tiles_kv <= 0) return BSA_ERR_MASK_SHAPE;
+    if ((int64_t)d.mask_tiles_q * kTile < d.max_seqlen_q) return BSA_ERR_MASK_SHAPE;
+    if (d.mask_tiles_kv > BSA_MAX_KV_TILES) return BSA_ERR_TOO_LARGE;
+  }
+  const int64_t grid = (int64_t)d.batch * d.num_heads_q * mt_grid;
+  if (grid > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
+  if (grid > 0) {
+    if (q == nullptr || kcache == nullptr || vcache == nullptr || qscale == nullptr ||
+        kscale == nullptr || vscale == nullptr || cu_seqlens_q == nullptr ||
+        block_table == nullptr || seqlens_kv == nullptr || out == nullptr)
+      return BSA_ERR_NULL_POINTER;
+  }
+  if (grid == 0) return BSA_OK;
+
+  Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.kc = static_cast<const uint8_t*>(kcache);
+  p.vc = static_cast<const uint8_t*>(vcache);
+  p.qscale = qscale;
+  p.kscale = kscale;
+  p.vscale = vscale;
+  p.cu_q = cu_seqlens_q;
+  p.block_table = block_table;
+  p.seqlens_kv = seqlens_kv;
+  p.mask = block_mask;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.B = d.batch;
+  p.T = d.total_q;
+  p.Hq = d.num_heads_q;
+  p.Hkv = d.num_heads_kv;
+  p.group = group;
+  p.page_size = page_size;
+  p.page_shift = page_size == 64 ? 6 : 5;
+  p.max_pages = d.max_pages_per_seq;
+  p.mt = d.mask_tiles_q;
+  p.mkv = d.mask_tiles_kv;
+  p.mt_grid = mt_grid;
+  p.layout = d.kv_layout;
+  p.causal = d.causal;
+  p.qk_scale = d.softmax_scale * kLog2e * kF16Widen;
+
+  if (quant_type == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR)
+    hipLaunchKernelGGL(bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR>,
+                       dim3((unsigned)grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
+  else
+    hipLaunchKernelGGL(bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD>,
+                       dim3((unsigned)grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
+  if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
+  return BSA_OK;
+}
+
+}  // extern "C"

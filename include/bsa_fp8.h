@@ -1,0 +1,157 @@
+/*
+ * bsa_fp8.h -- C ABI of the block-sparse FP8 (E4M3) attention prefill library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the attention formula of "Quant Block Sparse Attention",
+ * section "Operator introduction"; the block mask and its tiling from the
+ * hpc-ops block-sparse FP8 attention article, section "Block-sparse
+ * scheduling"):
+ *
+ *   for every sequence b, query head h and query t of that sequence,
+ *     Omega_t = { key j < Lkv_b : block_mask[b, h, t/128, j/128] != 0
+ *                                 and (causal ? j <= Lkv_b - Lq_b + t : true) }
+ *     score_j = softmax_scale * (q[t,h,:]*qscale[t,h]) . (k_j*kdescale_j)
+ *     out[t,h,:] = sum_{j in Omega_t} softmax_j(score) * v_j * vdescale_g
+ *     lse[h,t]   = ln sum_{j in Omega_t} exp(score_j)
+ *   with g = h / (Hq/Hkv).  An empty Omega_t gives out = 0 and
+ *   lse = -FLT_MAX ("Quant Block Sparse Attention", section "Sparse indices &
+ *   PA page table").  Causal alignment is bottom-right ("right-context causal",
+ *   its constraint table).
+ *
+ *   The probabilities of each 128-key tile, taken against the running row
+ *   maximum, are multiplied by 256 and rounded to E4M3 before the P.V product
+ *   (hpc-ops article, section "FP8 Tensor Core compute: fixed P-scale
+ *   quantisation"); the 1/256 is folded into the final normalisation together
+ *   with the V descale.  Active KV tiles are visited in ascending order; tiles
+ *   that the mask switches off are never read (hpc-ops article, section
+ *   "Active tile list").
+ *
+ * Ownership and threading
+ *   Every array argument is a DEVICE pointer owned by the caller.  The library
+ *   allocates no memory, never synchronises, and never reads device data on the
+ *   host: a call validates its static arguments on the host, then enqueues one
+ *   kernel on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *   Results are ready when that stream reaches the kernel.
+ *
+ * Errors
+ *   A call returns BSA_OK (0) or a positive bsa_status.  Static-argument errors
+ *   are detected before any HIP call; then nothing is enqueued and the outputs
+ *   are untouched.  BSA_ERR_LAUNCH means the HIP launch itself failed.
+ *   Data-dependent preconditions (listed below) are not checked, because the
+ *   host never reads device memory.
+ */
+#ifndef BSA_FP8_H
+#define BSA_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Quantisation schemes (hpc-ops article, section "FP8 Tensor Core compute",
+ * the two QuantType values; "Quant Block Sparse Attention", "Key parameters"). */
+typedef enum {
+    /* Q per (token, head); K per tensor; V per tensor.
+     * qscale float [T, Hq]; kscale float [1]; vscale float [1]. */
+    BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR = 0,
+    /* Q per (token, head); K per (token slot, kv-head); V per kv-head.
+     * qscale float [T, Hq]; kscale float laid out like the cache minus the
+     * head dimension: [num_pages, page_size, Hkv] (NHD) or
+     * [num_pages, Hkv, page_size] (HND); vscale float [Hkv]. */
+    BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD = 1
+} bsa_quant_type;
+
+/* Paged KV cache layouts (hpc-ops article, section "3.16x": NHD and HND). */
+typedef enum {
+    BSA_KV_NHD = 0, /* kcache/vcache E4M3 [num_pages, page_size, Hkv, 128] */
+    BSA_KV_HND = 1  /* kcache/vcache E4M3 [num_pages, Hkv, page_size, 128] */
+} bsa_kv_layout;
+
+typedef enum {
+    BSA_OK = 0,
+    BSA_ERR_NULL_POINTER = 1,  /* a required pointer (or dims) is NULL          */
+    BSA_ERR_HEAD_DIM = 2,      /* head_dim != 128                               */
+    BSA_ERR_PAGE_SIZE = 3,     /* page_size not 32 or 64                        */
+    BSA_ERR_GQA = 4,           /* Hq % Hkv != 0 or Hq/Hkv outside 1..16         */
+    BSA_ERR_QUANT_TYPE = 5,    /* quant_type not a bsa_quant_type               */
+    BSA_ERR_KV_LAYOUT = 6,     /* kv_layout not a bsa_kv_layout                 */
+    BSA_ERR_SIZE = 7,          /* a size is negative or inconsistent            */
+    BSA_ERR_MASK_SHAPE = 8,    /* mask_tiles_q * 128 < max_seqlen_q, or a mask
+                                  dimension is not positive                     */
+    BSA_ERR_SOFTMAX_SCALE = 9, /* softmax_scale not finite                      */
+    BSA_ERR_TOO_LARGE = 10,    /* mask_tiles_kv above BSA_MAX_KV_TILES, or a
+                                  grid dimension overflow                       */
+    BSA_ERR_LAUNCH = 11        /* the kernel launch failed                      */
+} bsa_status;
+
+/* Largest block-mask width (KV tiles of 128 keys) a masked call accepts:
+ * 4096 tiles = 524288 keys.  A call with block_mask == NULL has no limit. */
+#define BSA_MAX_KV_TILES 4096
+
+typedef struct {
+    int32_t batch;             /* B, number of sequences                        */
+    int32_t total_q;           /* T, packed query tokens (= cu_seqlens_q[B])   */
+    int32_t num_heads_q;       /* Hq                                            */
+    int32_t num_heads_kv;      /* Hkv; Hq % Hkv == 0, 1 <= Hq/Hkv <= 16         */
+    int32_t head_dim;          /* must be 128                                   */
+    int32_t num_pages;         /* physical pages in kcache / vcache             */
+    int32_t max_pages_per_seq; /* row length of block_table                     */
+    int32_t max_seqlen_q;      /* upper bound of every Lq_b (sets the grid)    */
+    int32_t mask_tiles_q;      /* block_mask dim 2 (max Q tiles per sequence)  */
+    int32_t mask_tiles_kv;     /* block_mask dim 3 (KV tiles, Kb)              */
+    int32_t kv_layout;         /* bsa_kv_layout                                 */
+    int32_t causal;            /* 1: bottom-right causal; 0: no causal mask    */
+    float softmax_scale;       /* usually 1/sqrt(128)                           */
+} bsa_fp8_dims;
+
+/*
+ * bsa_fp8_prefill -- block-sparse FP8 attention prefill over a paged KV cache.
+ *
+ * q            E4M3 [T, Hq, 128], packed varlen queries (TND).
+ * kcache,
+ * vcache       E4M3 paged caches, layout dims->kv_layout, page_size slots
+ *              per page.  Slots at or beyond Lkv_b may hold anything (NaN
+ *              included): they never contribute.
+ * qscale       float [T, Hq] Q descales (multiplied in).
+ * kscale,
+ * vscale       float, shapes per quant_type (see bsa_quant_type).
+ * cu_seqlens_q int32 [B+1], leading 0, non-decreasing, ends at T.
+ * block_table  int32 [B, max_pages_per_seq]: logical page -> physical page.
+ *              Only entries of pages that hold keys < Lkv_b are read.
+ * seqlens_kv   int32 [B], Lkv_b.
+ * block_mask   uint8 [B, Hq, mask_tiles_q, mask_tiles_kv], non-zero = compute
+ *              that (Q tile, KV tile) pair.  NULL = every tile (dense path).
+ *              Bits above the causal range, at or beyond Lkv_b, or on Q tiles
+ *              beyond Lq_b have no effect.
+ * quant_type   bsa_quant_type.
+ * page_size    32 or 64.
+ * dims         sizes and flags (host pointer).
+ * out          bf16 [T, Hq, 128] (TND), written for every query token.
+ * lse          float [Hq, T], natural-log LSE; may be NULL (not written).
+ * stream       hipStream_t to enqueue on.
+ *
+ * Preconditions the library cannot check (caller's contract):
+ *   Lq_b <= Lkv_b; max_seqlen_q >= every Lq_b; with a mask,
+ *   Lkv_b <= 128 * mask_tiles_kv (tiles beyond the mask width count as off);
+ *   block_table entries of pages holding keys < Lkv_b are valid page ids;
+ *   every descale is finite and >= 0.
+ */
+int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache,
+                    const float* qscale, const float* kscale, const float* vscale,
+                    const int32_t* cu_seqlens_q, const int32_t* block_table,
+                    const int32_t* seqlens_kv, const uint8_t* block_mask,
+                    int quant_type, int page_size, const bsa_fp8_dims* dims,
+                    void* out, float* lse, void* stream);
+
+/* Static text for a bsa_status value (never NULL). */
+const char* bsa_fp8_status_string(int status);
+
+/* Library ABI version, currently 1. */
+int bsa_fp8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_FP8_H */

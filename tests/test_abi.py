@@ -1,0 +1,136 @@
+"""The C ABI library: it loads without a GPU, exports every declared symbol, and
+rejects bad static arguments with the documented status before any HIP call."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_fp8_amd as bsa
+from block_sparse_fp8_amd import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa_fp8.h")
+CONSTRAINTS = json.load(open(os.path.join(ROOT, "tests", "golden", "constraints.json")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bsa.library_path()):
+        from block_sparse_fp8_amd import build
+        build.build()
+    return bsa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_fp8_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "bsa_fp8_prefill" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.bsa_fp8_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(0, 12):
+        assert isinstance(bsa.status_string(s), str) and bsa.status_string(s)
+    assert bsa.status_string(999) == "unknown status"
+
+
+def test_status_enum_matches_header():
+    text = open(HEADER).read()
+    vals = dict((k, int(v)) for k, v in re.findall(r"(BSA_(?:OK|ERR_\w+))\s*=\s*(\d+)", text))
+    assert vals["BSA_OK"] == 0
+    assert len(set(vals.values())) == len(vals)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def good_dims(**kw):
+    d = dict(batch=1, total_q=256, num_heads_q=8, num_heads_kv=2, head_dim=128, num_pages=8,
+             max_pages_per_seq=4, max_seqlen_q=256, mask_tiles_q=2, mask_tiles_kv=2, kv_layout=0,
+             causal=1, softmax_scale=0.08838834764831845)
+    d.update(kw)
+    return Dims(**d)
+
+
+def call(lib, dims, quant=0, page_size=64, mask=FAKE, q=FAKE, out=FAKE, dims_ptr=True):
+    return lib.bsa_fp8_prefill(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mask, quant,
+                               page_size, ctypes.byref(dims) if dims_ptr else None, out, FAKE, None)
+
+
+CASES = [
+    ("BSA_ERR_HEAD_DIM", dict(head_dim=64), {}),
+    ("BSA_ERR_HEAD_DIM", dict(head_dim=256), {}),
+    ("BSA_ERR_PAGE_SIZE", {}, dict(page_size=16)),
+    ("BSA_ERR_PAGE_SIZE", {}, dict(page_size=128)),
+    ("BSA_ERR_GQA", dict(num_heads_q=6, num_heads_kv=4), {}),
+    ("BSA_ERR_GQA", dict(num_heads_q=34, num_heads_kv=2), {}),
+    ("BSA_ERR_QUANT_TYPE", {}, dict(quant=2)),
+    ("BSA_ERR_QUANT_TYPE", {}, dict(quant=-1)),
+    ("BSA_ERR_KV_LAYOUT", dict(kv_layout=2), {}),
+    ("BSA_ERR_SIZE", dict(batch=-1), {}),
+    ("BSA_ERR_SIZE", dict(num_heads_kv=0), {}),
+    ("BSA_ERR_SIZE", dict(causal=3), {}),
+    ("BSA_ERR_MASK_SHAPE", dict(mask_tiles_q=1), {}),
+    ("BSA_ERR_MASK_SHAPE", dict(mask_tiles_kv=0), {}),
+    ("BSA_ERR_SOFTMAX_SCALE", dict(softmax_scale=float("nan")), {}),
+    ("BSA_ERR_SOFTMAX_SCALE", dict(softmax_scale=float("inf")), {}),
+    ("BSA_ERR_TOO_LARGE", dict(mask_tiles_kv=4097), {}),
+    ("BSA_ERR_NULL_POINTER", {}, dict(q=None)),
+    ("BSA_ERR_NULL_POINTER", {}, dict(out=None)),
+    ("BSA_ERR_NULL_POINTER", {}, dict(dims_ptr=False)),
+]
+
+
+def status_values():
+    text = open(HEADER).read()
+    return dict((k, int(v)) for k, v in re.findall(r"(BSA_(?:OK|ERR_\w+))\s*=\s*(\d+)", text))
+
+
+@pytest.mark.parametrize("name,dkw,ckw", CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(CASES)])
+def test_static_validation(lib, name, dkw, ckw):
+    assert call(lib, good_dims(**dkw), **ckw) == status_values()[name]
+
+
+def test_constraints_follow_the_pages(lib):
+    """head_dim 128 only, page sizes 32/64, GQA ratio 1..16 (constraint table)."""
+    st = status_values()
+    for ps in range(1, 129):
+        r = call(lib, good_dims(batch=0), page_size=ps)
+        assert (r == st["BSA_OK"]) == (ps in CONSTRAINTS["page_sizes"])
+    for ratio in range(1, 20):
+        r = call(lib, good_dims(batch=0, num_heads_q=ratio, num_heads_kv=1))
+        ok = CONSTRAINTS["gqa_ratio_min"] <= ratio <= CONSTRAINTS["gqa_ratio_max"]
+        assert (r == st["BSA_OK"]) == ok
+
+
+def test_empty_grid_returns_ok_without_launch(lib):
+    # batch = 0 or max_seqlen_q = 0: nothing to do, no HIP call, null pointers accepted
+    z = ctypes.c_void_p(0)
+    d = good_dims(batch=0)
+    assert lib.bsa_fp8_prefill(z, z, z, z, z, z, z, z, z, z, 0, 64, ctypes.byref(d), z, z, None) == 0
+    d = good_dims(max_seqlen_q=0, total_q=0)
+    assert lib.bsa_fp8_prefill(z, z, z, z, z, z, z, z, z, z, 0, 64, ctypes.byref(d), z, z, None) == 0
+
+
+def test_failed_call_leaves_outputs_untouched(lib):
+    out = np.full(64, 7, dtype=np.uint16)
+    r = call(lib, good_dims(head_dim=64), out=ctypes.c_void_p(out.ctypes.data))
+    assert r == status_values()["BSA_ERR_HEAD_DIM"]
+    assert np.all(out == 7)
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    x = torch.zeros(4, 2, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        bsa.bsa_fp8_prefill(x, x, x, x, x, x, x, x, x, None, 0, 64, max_seqlen_q=4)

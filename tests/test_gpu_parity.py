@@ -1,0 +1,172 @@
+"""GPU parity: the HIP kernel through the C ABI versus the fp64 oracle.
+
+Small shapes are compared on every output element; the five workload
+configurations at full size are compared on seeded samples of Q tiles (the
+launch is the full problem, exactly as the benchmark times it), plus
+properties that hold for every output element.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from synth import make_problem
+from synth.workloads import sample_q_tiles
+from parity_util import run_gpu, compare, tile_rows, NEG_FLT_MAX
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check(problem, tiles=None, mask=True, causal=None, label=""):
+    say(f"[gpu] {label} cfg={problem.cfg.name} lq={problem.cfg.lq} lkv={problem.cfg.lkv} "
+        f"hq={problem.cfg.hq} hkv={problem.cfg.hkv} quant={problem.quant_type} "
+        f"layout={problem.kv_layout} ps={problem.page_size} mask={mask} tiles={None if tiles is None else len(tiles)}")
+    go, gl = run_gpu(problem, mask=mask, causal=causal)
+    kw = problem.oracle_kwargs()
+    if not mask:
+        kw["block_mask"] = None
+    if causal is not None:
+        kw["causal"] = causal
+    eo, el = A.prefill(**kw, mode="emulate", tiles=tiles)
+    xo, _ = A.prefill(**kw, mode="exact", tiles=tiles)
+    sel = None if tiles is None else tile_rows(problem, tiles)
+    stats = compare(go, gl, eo, el, xo, sel)
+    say(f"[gpu]   ok {stats}")
+    return go, gl
+
+
+SMALL = [
+    dict(lq=(300,), lkv=(300,), hq=2, hkv=1, quant_type=0, kv_layout=0, page_size=64, keep=0.5),
+    dict(lq=(200, 77), lkv=(390, 77), hq=4, hkv=2, quant_type=1, kv_layout=1, page_size=32, keep=0.5),
+    dict(lq=(129,), lkv=(383,), hq=3, hkv=3, quant_type=1, kv_layout=0, page_size=32, keep=0.3),
+    dict(lq=(64, 256, 1), lkv=(250, 256, 700), hq=4, hkv=1, quant_type=0, kv_layout=1, page_size=64,
+         keep=0.7),
+    dict(lq=(1000,), lkv=(1500,), hq=16, hkv=1, quant_type=1, kv_layout=0, page_size=64, keep=0.4),
+]
+
+
+def test_tiny_config_all_elements():
+    check(make_problem("tiny"), label="tiny")
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("page_size", [32, 64])
+@pytest.mark.parametrize("quant", [0, 1])
+def test_layout_page_quant_matrix(layout, page_size, quant):
+    p = make_problem("tiny", kv_layout=layout, page_size=page_size, quant_type=quant)
+    check(p, label=f"matrix L{layout} P{page_size} Q{quant}")
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_small_shapes_all_elements(i):
+    check(make_problem("tiny", seed=50 + i, **SMALL[i]), label=f"small{i}")
+
+
+def test_skip_ratio_zero_and_null_mask():
+    p = make_problem("tiny", seed=9, **{**SMALL[1], "keep": 1.0})
+    p.block_mask[:] = 1
+    o1, l1 = check(p, label="all-ones mask")
+    o2, l2 = check(p, mask=False, label="NULL mask")
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_non_causal():
+    check(make_problem("tiny", seed=11, **SMALL[0]), causal=False, label="non-causal")
+    check(make_problem("tiny", seed=12, **SMALL[1]), causal=False, label="non-causal varlen")
+
+
+def test_empty_rows_exact():
+    p = make_problem("tiny", seed=13, **SMALL[1])
+    p.block_mask[1, 2, 0, :] = 0               # whole Q tile empty
+    p.block_mask[0, 1, 0, :] = 0               # only a future tile: early rows empty
+    p.block_mask[0, 1, 0, 2] = 1
+    go, gl = check(p, label="empty rows")
+    t0 = int(p.cu_seqlens_q[1])
+    assert np.all(go[t0:t0 + 77, 2] == 0.0)
+    assert np.all(gl[2, t0:t0 + 77] == NEG_FLT_MAX)
+    pos = 390 - 200 + np.arange(128)
+    assert np.all(gl[1, :128][pos < 256] == NEG_FLT_MAX)
+    assert np.all(gl[1, :128][pos >= 256] > NEG_FLT_MAX)
+
+
+def test_nan_in_unused_slots_and_spare_pages():
+    cfg = SMALL[4]
+    a = make_problem("tiny", seed=14, fill="zero", **cfg)
+    b = make_problem("tiny", seed=14, fill="nan", **cfg)
+    say("[gpu] nan-fill pair")
+    oa, la = run_gpu(a)
+    ob, lb = run_gpu(b)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_nan_in_skipped_pages():
+    cfg = dict(lq=(256,), lkv=(1024,), hq=4, hkv=2, quant_type=1, kv_layout=0, page_size=64, keep=1.0)
+    a = make_problem("tiny", seed=15, identity_pages=True, **cfg)
+    b = make_problem("tiny", seed=15, identity_pages=True, **cfg)
+    for p in (a, b):
+        p.block_mask[:, :, :, 2] = 0           # KV tile 2 (keys 256..383) off everywhere
+    b.kcache[4:6] = 0x7F                       # its pages hold NaN
+    b.vcache[4:6] = 0x7F
+    b.kscale[4:6] = np.nan
+    say("[gpu] nan skipped pages")
+    oa, la = run_gpu(a)
+    ob, lb = run_gpu(b)
+    assert np.all(np.isfinite(ob))
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_page_permutation_invariance():
+    a = make_problem("tiny", seed=16, identity_pages=True, **SMALL[3])
+    b = make_problem("tiny", seed=16, identity_pages=False, **SMALL[3])
+    say("[gpu] page permutation")
+    oa, la = run_gpu(a)
+    ob, lb = run_gpu(b)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_zero_q_closed_form():
+    p = make_problem("tiny", seed=17, **SMALL[1])
+    p.q[:] = 0
+    say("[gpu] Q=0 closed form")
+    go, gl = run_gpu(p)
+    eo, el = A.prefill(**p.oracle_kwargs(), mode="exact")
+    ok = el > NEG_FLT_MAX
+    # LSE = ln|Omega| exactly up to fp32 rounding; O = mean of V^ over Omega
+    np.testing.assert_allclose(gl[ok], el[ok], rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(go, eo, rtol=2 ** -7, atol=1e-4)
+
+
+def test_deterministic():
+    p = make_problem("tiny", seed=18, **SMALL[4])
+    say("[gpu] determinism")
+    o1, l1 = run_gpu(p)
+    o2, l2 = run_gpu(p)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+FULL = [("dense8k", 40, ()), ("sparse16k", 48, ()), ("varlen", 48, ((3, 5, 17), (0, 0, 0))),
+        ("long128k", 64, ((0, 0, 0), (0, 31, 1023), (0, 7, 1)))]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,count,must", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, count, must):
+    p = make_problem(name)
+    tiles = sample_q_tiles(p, count, seed=1, must_include=must)
+    go, gl = check(p, tiles=tiles, label=f"full {name}")
+    # properties of every element: finite, LSE finite or the empty marker
+    assert np.all(np.isfinite(go))
+    assert np.all(np.isfinite(gl))
+    if name == "varlen":
+        t0 = int(p.cu_seqlens_q[3])
+        rows = slice(t0 + 17 * 128, t0 + 18 * 128)
+        assert np.all(go[rows, 5] == 0.0)
+        assert np.all(gl[5, rows] == NEG_FLT_MAX)
