@@ -42,7 +42,9 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 #include <math.h>
+#include <string.h>
 
 #include "bsa_fp8.h"
 
@@ -104,12 +106,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // Four E4M3 codes (one dword) -> four f16 values holding code_value * 2^-8,
 // exactly (E4M3 subnormals land on f16 subnormals).  Returned as two dwords.
+// Per 16-bit half holding a code c in its low byte, (c + (c & 0x80)) << 7
+// moves the sign to bit 15 and the exponent/mantissa to bits 14..7.
 __device__ __forceinline__ v2i e4m3x4_to_f16x4(uint32_t w) {
-  // place codes in the high byte of each 16-bit half: [0,c0,0,c1] and [0,c2,0,c3]
-  const uint32_t lo = __builtin_amdgcn_perm(0u, w, 0x010c000cu);
-  const uint32_t hi = __builtin_amdgcn_perm(0u, w, 0x030c020cu);
-  const uint32_t flo = (lo & 0x80008000u) | ((lo >> 1) & 0x3f803f80u);
-  const uint32_t fhi = (hi & 0x80008000u) | ((hi >> 1) & 0x3f803f80u);
+  const uint32_t lo = __builtin_amdgcn_perm(0u, w, 0x0c010c00u);  // [c0,0,c1,0]
+  const uint32_t hi = __builtin_amdgcn_perm(0u, w, 0x0c030c02u);  // [c2,0,c3,0]
+  const uint32_t flo = (lo + (lo & 0x00800080u)) << 7;
+  const uint32_t fhi = (hi + (hi & 0x00800080u)) << 7;
   return v2i{(int)flo, (int)fhi};
 }
 
@@ -168,13 +171,22 @@ bsa_fp8_prefill_kernel(Params p) {
   const int hd = lane >> 5;   // lane half
   const int col = lane & 31;  // query column owned by this lane within the wave
 
-  // Heavy-first order: the largest Q-tile index (most causal work) first.
-  const int per_m = p.B * p.Hq;
-  const int m = p.mt_grid - 1 - (int)(blockIdx.x / per_m);
-  const int rem = (int)(blockIdx.x % per_m);
-  const int b = rem / p.Hq;
-  const int h = rem % p.Hq;
-  const int g = h / p.group;
+  // Work order.  The hardware hands consecutive workgroup ids to the 8 XCDs
+  // round-robin; id i is remapped so that XCD (i % 8) walks a contiguous slice
+  // of the logical list, which is ordered by kv-group (kv-head outer, sequence
+  // inner), then Q tile from the last (most causal work) down, then q-head
+  // within the group.  Each XCD's L2 then serves the K/V of its own kv-heads.
+  const int total = p.B * p.Hq * p.mt_grid;
+  const int per_xcd = total >> 3;
+  const int i = (int)blockIdx.x;
+  const int L = i < (per_xcd << 3) ? (i & 7) * per_xcd + (i >> 3) : i;
+  const int per_group = p.group * p.mt_grid;
+  const int gi = L / per_group;
+  const int within = L - gi * per_group;
+  const int m = p.mt_grid - 1 - within / p.group;
+  const int b = gi % p.B;
+  const int g = gi / p.B;
+  const int h = g * p.group + within % p.group;
 
   const int t0 = p.cu_q[b];
   const int lq = p.cu_q[b + 1] - t0;
@@ -226,6 +238,10 @@ bsa_fp8_prefill_kernel(Params p) {
     }
   }
   if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR) cscale *= p.kscale[0];
+  // Keep the score constant strictly positive so that a masked score (-inf)
+  // maps to exp2(-inf) = 0 without a select.  With descales >= 0 this only
+  // changes a zero constant, where every x is then ~1e-38 * S instead of 0.
+  cscale = fmaxf(cscale, 1.17549435e-38f);
   const float vdesc = QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR ? p.vscale[0] : p.vscale[g];
 
   v16f oacc[4];
@@ -282,10 +298,11 @@ bsa_fp8_prefill_kernel(Params p) {
   };
 
   int n = walk.next(lane);
-  int buf = 0;
   if (n >= 0) issue_tile(n, 0);
 
-  while (n >= 0) {
+  // One active tile; BUF is the LDS buffer holding its V (and K descales).
+  auto tile_step = [&](auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // k16 and the other V buffer are no longer read; this tile's V is in LDS
     // Widen this tile's K to f16 in LDS.  Layout is chunk-major: the 16-byte
@@ -365,16 +382,11 @@ bsa_fp8_prefill_kernel(Params p) {
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
-        float e0 = __builtin_amdgcn_exp2f(fmaf(s[c][r], cscale, bias));
-        float e1 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 1], cscale, bias));
-        float e2 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 2], cscale, bias));
-        float e3 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 3], cscale, bias));
-        if (band) {
-          e0 = s[c][r] == -INFINITY ? 0.0f : e0;
-          e1 = s[c][r + 1] == -INFINITY ? 0.0f : e1;
-          e2 = s[c][r + 2] == -INFINITY ? 0.0f : e2;
-          e3 = s[c][r + 3] == -INFINITY ? 0.0f : e3;
-        }
+        // masked scores are -inf and cscale > 0, so their P' is exactly 0
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[c][r], cscale, bias));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 1], cscale, bias));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 2], cscale, bias));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 3], cscale, bias));
         lsum += (e0 + e1) + (e2 + e3);
         // bytes (c&1)*16 + r .. +3 of the P operand of PV step c>>1
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
@@ -419,7 +431,11 @@ bsa_fp8_prefill_kernel(Params p) {
       }
     }
     n = n_next;
-    buf ^= 1;
+  };
+  while (n >= 0) {
+    tile_step(std::integral_constant<int, 0>{});
+    if (n < 0) break;
+    tile_step(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -489,9 +505,11 @@ int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache, const
   if (d.num_heads_q % d.num_heads_kv != 0) return BSA_ERR_GQA;
   const int group = d.num_heads_q / d.num_heads_kv;
   if (group < 1 || group > 16) return BSA_ERR_GQA;
-  if (!(d.softmax_scale == d.softmax_scale) || d.softmax_scale == INFINITY ||
-      d.softmax_scale == -INFINITY)
-    return BSA_ERR_SOFTMAX_SCALE;
+  {
+    uint32_t bits;
+    memcpy(&bits, &d.softmax_scale, sizeof(bits));
+    if ((bits & 0x7f800000u) == 0x7f800000u) return BSA_ERR_SOFTMAX_SCALE;  // inf or NaN
+  }
   if (d.causal != 0 && d.causal != 1) return BSA_ERR_SIZE;
   const int mt_grid = (d.max_seqlen_q + kTile - 1) / kTile;
   if (block_mask != nullptr) {
