@@ -265,40 +265,70 @@ bsa_fp8_prefill_kernel(Params p) {
   const int khalf = tid >> 7;
   v4i kreg[4];
 
-  auto issue_tile = [&](int n, int buf) {
-    {
-      const int j = n * kTile + krow_ld;
-      if (j < lkv) {
-        const int64_t r = kv_row_index(p, bt[j >> p.page_shift], j & (p.page_size - 1), g);
-        const v4i* src = reinterpret_cast<const v4i*>(p.kc + r * kHeadDim + khalf * 64);
+  // Loads of a tile come in three parts, spread over iterations so that no
+  // memory latency sits on the critical path:
+  //  * lookup(n): the page-table entries of tile n, issued two tiles ahead and
+  //    waited only at the top of the next iteration (the VMEM counter drains
+  //    in order, so a lookup waited right before the data loads that need it
+  //    would expose a full memory round trip every tile);
+  //  * issue_k(n): the K rows of tile n into registers, one tile ahead;
+  //  * issue_v(n): the V rows (and per-token K descales) of tile n straight
+  //    into LDS, issued after the current tile's PV so that no direct-to-LDS
+  //    load is in flight while LDS operands are read (the compiler can then
+  //    wait for exact LDS counts).
+  // Rows past the KV length are redirected to row lkv-1 (valid; every lookup
+  // index is at most (lkv-1)/page_size): their K is zeroed and their P is 0.
+  // The 32 V rows of a wave lie in one 32-aligned block, hence in one page.
+  struct PageSet {
+    int k, v, ks;
+  };
+  auto lookup = [&](int n) -> PageSet {
+    PageSet ps;
+    ps.k = bt[min(n * kTile + krow_ld, lkv - 1) >> p.page_shift];
+    ps.v = bt[min(n * kTile + wave * 32, lkv - 1) >> p.page_shift];
+    ps.ks = QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD
+                ? bt[min(n * kTile + (wave & 1) * 64 + lane, lkv - 1) >> p.page_shift]
+                : 0;
+    return ps;
+  };
+  // (rows past the KV length are zeroed when K is widened, not here: a select
+  // on the loaded registers would make the loads complete at once)
+  auto issue_k = [&](int n, const PageSet& ps) {
+    const int64_t r = kv_row_index(p, ps.k, min(n * kTile + krow_ld, lkv - 1) & (p.page_size - 1), g);
+    const v4i* src = reinterpret_cast<const v4i*>(p.kc + r * kHeadDim + khalf * 64);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kreg[i] = src[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kreg[i] = v4i{0, 0, 0, 0};
-      }
-    }
+    for (int i = 0; i < 4; ++i) kreg[i] = src[i];
+  };
+  auto issue_v = [&](int n, int buf, const PageSet& ps) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wave * 32 + i * 8 + (lane >> 3);
-      const int pchunk = lane & 7;
-      int j = n * kTile + row;
-      if (j >= lkv) j = n * kTile;  // rows past the KV length read a valid row; P is 0 there
-      const int64_t r = kv_row_index(p, bt[j >> p.page_shift], j & (p.page_size - 1), g);
-      const uint8_t* src = p.vc + r * kHeadDim + ((pchunk ^ swz8(row)) << 4);
+      const int j = min(n * kTile + row, lkv - 1);
+      const int64_t r = kv_row_index(p, ps.v, j & (p.page_size - 1), g);
+      const uint8_t* src = p.vc + r * kHeadDim + (((lane & 7) ^ swz8(row)) << 4);
       __builtin_amdgcn_global_load_lds((glb_void*)src,
                                        (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
     }
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD && wave < 2) {
-      int j = n * kTile + wave * 64 + lane;
-      if (j >= lkv) j = n * kTile;
-      const int64_t r = kv_row_index(p, bt[j >> p.page_shift], j & (p.page_size - 1), g);
+      const int j = min(n * kTile + wave * 64 + lane, lkv - 1);
+      const int64_t r = kv_row_index(p, ps.ks, j & (p.page_size - 1), g);
       __builtin_amdgcn_global_load_lds((glb_void*)(p.kscale + r), (lds_void*)(&ks_lds[buf][wave * 64]), 4, 0, 0);
     }
   };
 
+  // n: tile being processed (LDS buffer parity `buf` of the step); n1: the
+  // next one.  Page ids live in pg[parity of the tile's position], so no copy
+  // of a pending load result is ever needed.
   int n = walk.next(lane);
-  if (n >= 0) issue_tile(n, 0);
+  int n1 = -1;
+  PageSet pg[2] = {{0, 0, 0}, {0, 0, 0}};
+  if (n >= 0) {
+    pg[0] = lookup(n);
+    issue_k(n, pg[0]);
+    issue_v(n, 0, pg[0]);
+    n1 = walk.next(lane);
+    if (n1 >= 0) pg[1] = lookup(n1);
+  }
 
   // One active tile; BUF is the LDS buffer holding its V (and K descales).
   auto tile_step = [&](auto buf_tag) {
@@ -307,6 +337,10 @@ bsa_fp8_prefill_kernel(Params p) {
     __syncthreads();  // k16 and the other V buffer are no longer read; this tile's V is in LDS
     // Widen this tile's K to f16 in LDS.  Layout is chunk-major: the 16-byte
     // chunk c (head-dim elements 8c..8c+7) of key row r sits at c*2048 + r*16.
+    if (n * kTile + krow_ld >= lkv) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kreg[i] = v4i{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const v2i a = e4m3x4_to_f16x4((uint32_t)kreg[i][0]);
@@ -318,24 +352,44 @@ bsa_fp8_prefill_kernel(Params p) {
       *reinterpret_cast<v4i*>(k16_lds + (chunk + 1) * 2048 + krow_ld * 16) = v4i{d[0], d[1], e[0], e[1]};
     }
     __syncthreads();  // k16 ready
-    const int n_next = walk.next(lane);
-    if (n_next >= 0) issue_tile(n_next, buf ^ 1);
+    if (n1 >= 0) issue_k(n1, pg[buf ^ 1]);
+    const int n2 = n1 >= 0 ? walk.next(lane) : -1;
+    if (n2 >= 0) pg[buf] = lookup(n2);
 
     // ---- S^T = K . Q^T (f16 operands, fp32 accumulation) ------------------
+    // k-step outer, 32-key block inner: four independent accumulation chains,
+    // and the operands of step ks+1 are read from LDS before the products of
+    // step ks are issued, so LDS latency hides behind the matrix pipe.
     v16f s[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int krow = (c >> 1) * 64 + hi_a * 32 + (c & 1) * 16 + ri_a;
-      const uint8_t* kp = k16_lds + hd * 2048 + krow * 16;
-      v16f acc;
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) s[c][r] = 0.0f;
+    {
+      const uint8_t* kp = k16_lds + hd * 2048 + (hi_a * 32 + ri_a) * 16;
+      auto kaddr = [&](int c, int ks) { return kp + ((c >> 1) * 64 + (c & 1) * 16) * 16 + ks * 4096; };
+      v8h acur[4], anxt[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acur[c] = *reinterpret_cast<const v8h*>(kaddr(c, 0));
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const v8h a = *reinterpret_cast<const v8h*>(kp + ks * 4096);
-        acc = mfma_f16(a, qh[ks], acc);
+        if (ks < 7) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) anxt[c] = *reinterpret_cast<const v8h*>(kaddr(c, ks + 1));
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[c] = mfma_f16(acur[c], qh[ks], s[c]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acur[c] = anxt[c];
       }
-      s[c] = acc;
+      // Keep four operand reads in flight ahead of the matrix products.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // DS read
+#pragma unroll
+      for (int k = 0; k < 14; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -430,7 +484,9 @@ bsa_fp8_prefill_kernel(Params p) {
         oacc[d] = mfma_f8(a, pk[sp], oacc[d]);
       }
     }
-    n = n_next;
+    if (n1 >= 0) issue_v(n1, buf ^ 1, pg[buf ^ 1]);
+    n = n1;
+    n1 = n2;
   };
   while (n >= 0) {
     tile_step(std::integral_constant<int, 0>{});
