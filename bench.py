@@ -14,6 +14,9 @@ FLOP for Q.K^T plus the same for P.V, i.e. 8,388,608 FLOP, and reads 32 KiB
 of K and V (plus 512 B of K descales with per-token K scales).
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +33,60 @@ KV_BYTES_PER_TILE = 2 * TILE * TILE             # 32,768
 PEAK_FP8_TFLOPS = 5000.0                        # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0
 METRIC = "effective FP8 TFLOPS (active tiles) + prefill tokens/s; % of FP8 MFMA peak"
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_fp8_amd", "csrc", "bsa_fp8_prefill.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 256 * 1024 * 1024   # size of the calibration copy (see --ingest-counters)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of
+    this exact kernel source, or None when there is no record or the kernel
+    source changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def _counter_means(directory, kernel_substr):
+    vals = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(path)):
+            if kernel_substr in row["Kernel_Name"]:
+                vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def ingest_counters(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command):
+    """Record FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the prefill kernel,
+    scaled by what the same counters read for a plain copy of COPY_BYTES."""
+    f = _counter_means(fetch_dir, "bsa_fp8_prefill_kernel")["FETCH_SIZE"]
+    w = _counter_means(write_dir, "bsa_fp8_prefill_kernel")["WRITE_SIZE"]
+    cf = _counter_means(cal_fetch_dir, "copyBuffer")["FETCH_SIZE"]
+    cw = _counter_means(cal_write_dir, "copyBuffer")["WRITE_SIZE"]
+    fetch_scale = COPY_BYTES / (cf * 1024)
+    write_scale = COPY_BYTES / (cw * 1024)
+    rec = {"kernel_source_sha256": kernel_source_hash(),
+           "fetch_kib_per_launch": f, "write_kib_per_launch": w,
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "hbm_bytes_per_launch": f * 1024 * fetch_scale + w * 1024 * write_scale,
+           "command": command}
+    try:
+        allrec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+    print(json.dumps(rec))
 
 
 def active_tiles(p):
@@ -106,7 +163,24 @@ def main():
     ap.add_argument("--workload", default="sparse16k")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="record HBM traffic of --workload from rocprofv3 counter CSV directories and exit")
+    ap.add_argument("--ingest-command", default="", help="command line recorded with --ingest-counters")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 256 MiB (x3), for calibrating FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        x = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copied_bytes": COPY_BYTES, "copies": 3}))
+        return
+    if args.ingest_counters:
+        ingest_counters(args.workload, *args.ingest_counters, command=args.ingest_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the kernel shards by kv-head with no communication; see the design notes)",
@@ -174,7 +248,7 @@ def main():
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic(p.cfg.name)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, n_act, args.cpu_budget)
