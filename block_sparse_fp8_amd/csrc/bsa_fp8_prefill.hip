@@ -141,7 +141,8 @@ struct TileWalk {
     bits = load_chunk(lane);
   }
   __device__ uint64_t load_chunk(int lane) const {
-    const int n = base + lane;
+    int n = base + lane;
+    asm volatile("" : "+v"(n));  // no per-lane pointer kept live across the tile loop
     const bool act = n < n_end && (row == nullptr || row[n] != 0);
     return __ballot(act);
   }
@@ -167,7 +168,7 @@ bsa_fp8_prefill_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hd = lane >> 5;   // lane half
   const int col = lane & 31;  // query column owned by this lane within the wave
 
@@ -211,7 +212,6 @@ bsa_fp8_prefill_kernel(Params p) {
   // Queries of this lane.
   const int tq = m * kTile + wave * 32 + col;             // query index within the sequence
   const bool q_valid = tq < lq;
-  const int p_pos = lkv - lq + tq;                        // causal position of this query
   const int p_wave_min = lkv - lq + m * kTile + wave * 32;  // smallest position in the wave
 
   // Q operand (B of S^T = K.Q^T, f16 32x32x16): lane holds query `col`,
@@ -254,15 +254,12 @@ bsa_fp8_prefill_kernel(Params p) {
 
   // K operand rows: accumulator row i of block c holds key
   // (c>>1)*64 + hi*32 + (c&1)*16 + ri with hi = (i>>2)&1, ri = (i>>3)*4 + (i&3).
-  const int hi_a = (col >> 2) & 1;
-  const int ri_a = ((col >> 3) << 2) | (col & 3);
 
   // Staging roles: K through registers, one row per thread (row tid & 127,
   // head-dim bytes 64*(tid>>7) .. +63); V by direct-to-LDS loads (wave w: rows
   // 32w..32w+31, 8 rows of 128 bytes per instruction).
   const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
-  const int krow_ld = tid & (kTile - 1);
-  const int khalf = tid >> 7;
+  const int khalf = wave >> 1;
   v4i kreg[4];
 
   // Loads of a tile come in three parts, spread over iterations so that no
@@ -282,35 +279,36 @@ bsa_fp8_prefill_kernel(Params p) {
   struct PageSet {
     int k, v, ks;
   };
-  auto lookup = [&](int n) -> PageSet {
+  // K row staged by this thread: (wave & 1) * 64 + lane.
+  auto lookup = [&](int n, int ln) -> PageSet {
     PageSet ps;
-    ps.k = bt[min(n * kTile + krow_ld, lkv - 1) >> p.page_shift];
+    ps.k = bt[min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) >> p.page_shift];
     ps.v = bt[min(n * kTile + wave * 32, lkv - 1) >> p.page_shift];
     ps.ks = QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD
-                ? bt[min(n * kTile + (wave & 1) * 64 + lane, lkv - 1) >> p.page_shift]
+                ? bt[min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) >> p.page_shift]
                 : 0;
     return ps;
   };
   // (rows past the KV length are zeroed when K is widened, not here: a select
   // on the loaded registers would make the loads complete at once)
-  auto issue_k = [&](int n, const PageSet& ps) {
-    const int64_t r = kv_row_index(p, ps.k, min(n * kTile + krow_ld, lkv - 1) & (p.page_size - 1), g);
+  auto issue_k = [&](int n, const PageSet& ps, int ln) {
+    const int64_t r = kv_row_index(p, ps.k, min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) & (p.page_size - 1), g);
     const v4i* src = reinterpret_cast<const v4i*>(p.kc + r * kHeadDim + khalf * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kreg[i] = src[i];
   };
-  auto issue_v = [&](int n, int buf, const PageSet& ps) {
+  auto issue_v = [&](int n, int buf, const PageSet& ps, int ln) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = wave * 32 + i * 8 + (lane >> 3);
+      const int row = wave * 32 + i * 8 + (ln >> 3);
       const int j = min(n * kTile + row, lkv - 1);
       const int64_t r = kv_row_index(p, ps.v, j & (p.page_size - 1), g);
-      const uint8_t* src = p.vc + r * kHeadDim + (((lane & 7) ^ swz8(row)) << 4);
+      const uint8_t* src = p.vc + r * kHeadDim + (((ln & 7) ^ swz8(row)) << 4);
       __builtin_amdgcn_global_load_lds((glb_void*)src,
                                        (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
     }
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD && wave < 2) {
-      const int j = min(n * kTile + wave * 64 + lane, lkv - 1);
+      const int j = min(n * kTile + wave * 64 + ln, lkv - 1);
       const int64_t r = kv_row_index(p, ps.ks, j & (p.page_size - 1), g);
       __builtin_amdgcn_global_load_lds((glb_void*)(p.kscale + r), (lds_void*)(&ks_lds[buf][wave * 64]), 4, 0, 0);
     }
@@ -323,21 +321,28 @@ bsa_fp8_prefill_kernel(Params p) {
   int n1 = -1;
   PageSet pg[2] = {{0, 0, 0}, {0, 0, 0}};
   if (n >= 0) {
-    pg[0] = lookup(n);
-    issue_k(n, pg[0]);
-    issue_v(n, 0, pg[0]);
+    pg[0] = lookup(n, lane);
+    issue_k(n, pg[0], lane);
+    issue_v(n, 0, pg[0], lane);
     n1 = walk.next(lane);
-    if (n1 >= 0) pg[1] = lookup(n1);
+    if (n1 >= 0) pg[1] = lookup(n1, lane);
   }
 
   // One active tile; BUF is the LDS buffer holding its V (and K descales).
   auto tile_step = [&](auto buf_tag) {
     constexpr int buf = decltype(buf_tag)::value;
+    // Lane-derived offsets are recomputed from an opaque copy of the lane id
+    // every tile instead of being held in registers across the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lhd = ln >> 5;
+    const int lcol = ln & 31;
+    const int krow = (wave & 1) * 64 + ln;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // k16 and the other V buffer are no longer read; this tile's V is in LDS
     // Widen this tile's K to f16 in LDS.  Layout is chunk-major: the 16-byte
     // chunk c (head-dim elements 8c..8c+7) of key row r sits at c*2048 + r*16.
-    if (n * kTile + krow_ld >= lkv) {
+    if (n * kTile + krow >= lkv) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) kreg[i] = v4i{0, 0, 0, 0};
     }
@@ -348,13 +353,13 @@ bsa_fp8_prefill_kernel(Params p) {
       const v2i d = e4m3x4_to_f16x4((uint32_t)kreg[i][2]);
       const v2i e = e4m3x4_to_f16x4((uint32_t)kreg[i][3]);
       const int chunk = 8 * khalf + 2 * i;
-      *reinterpret_cast<v4i*>(k16_lds + chunk * 2048 + krow_ld * 16) = v4i{a[0], a[1], c[0], c[1]};
-      *reinterpret_cast<v4i*>(k16_lds + (chunk + 1) * 2048 + krow_ld * 16) = v4i{d[0], d[1], e[0], e[1]};
+      *reinterpret_cast<v4i*>(k16_lds + chunk * 2048 + krow * 16) = v4i{a[0], a[1], c[0], c[1]};
+      *reinterpret_cast<v4i*>(k16_lds + (chunk + 1) * 2048 + krow * 16) = v4i{d[0], d[1], e[0], e[1]};
     }
     __syncthreads();  // k16 ready
-    if (n1 >= 0) issue_k(n1, pg[buf ^ 1]);
-    const int n2 = n1 >= 0 ? walk.next(lane) : -1;
-    if (n2 >= 0) pg[buf] = lookup(n2);
+    if (n1 >= 0) issue_k(n1, pg[buf ^ 1], ln);
+    const int n2 = n1 >= 0 ? walk.next(ln) : -1;
+    if (n2 >= 0) pg[buf] = lookup(n2, ln);
 
     // ---- S^T = K . Q^T (f16 operands, fp32 accumulation) ------------------
     // k-step outer, 32-key block inner: four independent accumulation chains,
@@ -366,7 +371,9 @@ bsa_fp8_prefill_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[c][r] = 0.0f;
     {
-      const uint8_t* kp = k16_lds + hd * 2048 + (hi_a * 32 + ri_a) * 16;
+      const int hi_a = (lcol >> 2) & 1;
+      const int ri_a = ((lcol >> 3) << 2) | (lcol & 3);
+      const uint8_t* kp = k16_lds + lhd * 2048 + (hi_a * 32 + ri_a) * 16;
       auto kaddr = [&](int c, int ks) { return kp + ((c >> 1) * 64 + (c & 1) * 16) * 16 + ks * 4096; };
       v8h acur[4], anxt[4];
 #pragma unroll
@@ -397,7 +404,7 @@ bsa_fp8_prefill_kernel(Params p) {
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float* ksp = &ks_lds[buf][(c >> 1) * 64 + hd * 32 + (c & 1) * 16];
+        const float* ksp = &ks_lds[buf][(c >> 1) * 64 + lhd * 32 + (c & 1) * 16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[c][r] *= ksp[r];
         __builtin_amdgcn_sched_barrier(0);
@@ -409,8 +416,8 @@ bsa_fp8_prefill_kernel(Params p) {
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = n * kTile + (c >> 1) * 64 + hd * 32 + (c & 1) * 16 + r;
-          const bool ok = j < lkv && (!p.causal || j <= p_pos);
+          const int j = n * kTile + (c >> 1) * 64 + lhd * 32 + (c & 1) * 16 + r;
+          const bool ok = j < lkv && (!p.causal || j <= p_wave_min + lcol);
           s[c][r] = ok ? s[c][r] : -INFINITY;
         }
     }
@@ -421,7 +428,11 @@ bsa_fp8_prefill_kernel(Params p) {
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) tmax = max3f(tmax, s[c][r], s[c][r + 1]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    {
+      // other lane half (keys of the other 32-row halves): v_permlane32_swap
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float tmax_x = tmax == -INFINITY ? -INFINITY : tmax * cscale;
     const float m_new = fmaxf(m_run, tmax_x);
     const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
@@ -461,30 +472,42 @@ bsa_fp8_prefill_kernel(Params p) {
     // Transposing read: in each 16-lane group, source lane 2k+q addresses key
     // row (step*64 + half*32 + 8*rr + k) at head-dim column base + 8q; result
     // lane i then holds column base + i for those 8 keys.
-    const int grp = lane >> 4;
-    const int il = lane & 15;
-    const int kk = il >> 1;
-    const int qq = il & 1;
+    // Rows sp*64 + half*32 + 8*rr + kk all share this lane's chunk swizzle, so
+    // one base per head-dim block d serves the whole tile.
+    const int grp = ln >> 4;
+    const int kk = (ln & 15) >> 1;
     const int half = grp >> 1;
-    const uint8_t* vbase = v8_lds[buf];
+    const int csw = (grp & 1) ^ kk ^ (half << 2);  // logical chunk 2d + (grp&1), swizzled
+    const uint8_t* vrow0 = v8_lds[buf] + (half * 32 + kk) * kHeadDim + 8 * (ln & 1);
+    auto vread = [&](int x) -> v8i {  // x = sp*4 + d
+      const uint8_t* vp = vrow0 + (((2 * (x & 3)) ^ csw) << 4) + (x >> 2) * 64 * kHeadDim;
+      v8i a;
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int chunk = 2 * d + (grp & 1);
-        v8i a;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int vrow = sp * 64 + half * 32 + 8 * rr + kk;
-          const int off = vrow * kHeadDim + ((chunk ^ swz8(vrow)) << 4) + 8 * qq;
-          const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vbase + off));
-          a[2 * rr] = t[0];
-          a[2 * rr + 1] = t[1];
-        }
-        oacc[d] = mfma_f8(a, pk[sp], oacc[d]);
+      for (int rr = 0; rr < 4; ++rr) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vp + rr * 8 * kHeadDim));
+        a[2 * rr] = t[0];
+        a[2 * rr + 1] = t[1];
       }
+      return a;
+    };
+    {
+      // operands of the next product are read while the current one runs
+      v8i va[8];
+      va[0] = vread(0);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        if (x + 1 < 8) va[x + 1] = vread(x + 1);
+        oacc[x & 3] = mfma_f8(va[x], pk[x >> 2], oacc[x & 3]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // DS read
+#pragma unroll
+      for (int k = 0; k < 7; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    if (n1 >= 0) issue_v(n1, buf ^ 1, pg[buf ^ 1]);
+    if (n1 >= 0) issue_v(n1, buf ^ 1, pg[buf ^ 1], ln);
     n = n1;
     n1 = n2;
   };
