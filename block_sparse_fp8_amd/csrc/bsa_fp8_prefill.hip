@@ -57,7 +57,6 @@ constexpr int kK16Row = 2 * kHeadDim;  // bytes per f16 K row in LDS
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kPScaleLog2 = 8.0f;      // P is scaled by 2^8 = 256 before rounding to E4M3
-constexpr float kF16Widen = 65536.0f;    // undoes the 2^-8 of the f16 widening of Q and of K
 constexpr float kNegFltMax = -3.402823466e+38f;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -87,16 +86,15 @@ struct Params {
   int page_size, page_shift, max_pages;
   int mt, mkv, mt_grid;
   int layout, causal;
-  float qk_scale;  // softmax_scale * log2(e) * 2^16
+  float qk_scale;       // softmax_scale * log2(e)
+  uint32_t page_bytes;  // bytes of one page of K (or V) cache: page_size * Hkv * 128
+  int slot_stride;      // rows between consecutive slots of a page (Hkv for NHD, 1 for HND)
+  int head_stride;      // rows between consecutive kv-heads of a page (1 for NHD, page_size for HND)
 };
 
 // 16-byte chunk swizzle of the fp8 V rows (128 B, 8 chunks) in LDS.
 __device__ __forceinline__ int swz8(int row) { return (row & 7) ^ (((row >> 5) & 1) << 2); }
 
-__device__ __forceinline__ int64_t kv_row_index(const Params& p, int page, int slot, int g) {
-  return p.layout == BSA_KV_NHD ? ((int64_t)page * p.page_size + slot) * p.Hkv + g
-                                : ((int64_t)page * p.Hkv + g) * p.page_size + slot;
-}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -104,16 +102,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Four E4M3 codes (one dword) -> four f16 values holding code_value * 2^-8,
-// exactly (E4M3 subnormals land on f16 subnormals).  Returned as two dwords.
-// Per 16-bit half holding a code c in its low byte, (c + (c & 0x80)) << 7
-// moves the sign to bit 15 and the exponent/mantissa to bits 14..7.
+// Four E4M3 codes (one dword) -> four f16 values, exactly (every E4M3 value,
+// subnormals included, is an f16 normal).  Returned as two dwords.
 __device__ __forceinline__ v2i e4m3x4_to_f16x4(uint32_t w) {
-  const uint32_t lo = __builtin_amdgcn_perm(0u, w, 0x0c010c00u);  // [c0,0,c1,0]
-  const uint32_t hi = __builtin_amdgcn_perm(0u, w, 0x0c030c02u);  // [c2,0,c3,0]
-  const uint32_t flo = (lo + (lo & 0x00800080u)) << 7;
-  const uint32_t fhi = (hi + (hi & 0x00800080u)) << 7;
-  return v2i{(int)flo, (int)fhi};
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  return v2i{(int)lo, (int)hi};
 }
 
 __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
@@ -289,28 +283,45 @@ bsa_fp8_prefill_kernel(Params p) {
                 : 0;
     return ps;
   };
+  // Byte offset of (page, slot, this kv-head) in a cache: one 32x32->64-bit
+  // product per page plus 32-bit in-page arithmetic.
+  const int head_row = g * p.head_stride;
+  auto row_addr = [&](const uint8_t* base, int pg, int slot) -> const uint8_t* {
+    return base + (uint64_t)(uint32_t)pg * p.page_bytes + (uint32_t)(slot * p.slot_stride + head_row) * kHeadDim;
+  };
+  const int pmask = p.page_size - 1;
   // (rows past the KV length are zeroed when K is widened, not here: a select
   // on the loaded registers would make the loads complete at once)
   auto issue_k = [&](int n, const PageSet& ps, int ln) {
-    const int64_t r = kv_row_index(p, ps.k, min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) & (p.page_size - 1), g);
-    const v4i* src = reinterpret_cast<const v4i*>(p.kc + r * kHeadDim + khalf * 64);
+    const int slot = min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) & pmask;
+    const v4i* src = reinterpret_cast<const v4i*>(row_addr(p.kc, ps.k, slot) + khalf * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kreg[i] = src[i];
   };
   auto issue_v = [&](int n, int buf, const PageSet& ps, int ln) {
+    const int row0 = wave * 32 + (ln >> 3);
+    if (n * kTile + kTile <= lkv) {
+      // Whole tile inside the KV length: the wave's 32 rows are consecutive
+      // slots of one page.
+      const uint8_t* src0 = row_addr(p.vc, ps.v, (n * kTile + row0) & pmask);
+      const uint32_t step = 8u * (uint32_t)p.slot_stride * kHeadDim;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wave * 32 + i * 8 + (ln >> 3);
-      const int j = min(n * kTile + row, lkv - 1);
-      const int64_t r = kv_row_index(p, ps.v, j & (p.page_size - 1), g);
-      const uint8_t* src = p.vc + r * kHeadDim + (((ln & 7) ^ swz8(row)) << 4);
-      __builtin_amdgcn_global_load_lds((glb_void*)src,
-                                       (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((glb_void*)(src0 + i * step + (((ln & 7) ^ swz8(row0 + i * 8)) << 4)),
+                                         (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = row0 + i * 8;
+        const int j = min(n * kTile + row, lkv - 1);
+        const uint8_t* src = row_addr(p.vc, ps.v, j & pmask) + (((ln & 7) ^ swz8(row)) << 4);
+        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
+      }
     }
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD && wave < 2) {
-      const int j = min(n * kTile + wave * 64 + ln, lkv - 1);
-      const int64_t r = kv_row_index(p, ps.ks, j & (p.page_size - 1), g);
-      __builtin_amdgcn_global_load_lds((glb_void*)(p.kscale + r), (lds_void*)(&ks_lds[buf][wave * 64]), 4, 0, 0);
+      const int slot = min(n * kTile + wave * 64 + ln, lkv - 1) & pmask;
+      const float* src = p.kscale + (uint64_t)(uint32_t)ps.ks * (p.page_bytes / kHeadDim) + (uint32_t)(slot * p.slot_stride + head_row);
+      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&ks_lds[buf][wave * 64]), 4, 0, 0);
     }
   };
 
@@ -423,11 +434,15 @@ bsa_fp8_prefill_kernel(Params p) {
     }
 
     // ---- online softmax ------------------------------------------------------
-    float tmax = -INFINITY;
+    // row max as a tree (eight independent partial maxima)
+    float pm[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) tmax = max3f(tmax, s[c][r], s[c][r + 1]);
+    for (int q8 = 0; q8 < 8; ++q8) {
+      const int c = q8 >> 1, r0 = (q8 & 1) * 8;
+      pm[q8] = max3f(max3f(s[c][r0], s[c][r0 + 1], s[c][r0 + 2]), max3f(s[c][r0 + 3], s[c][r0 + 4], s[c][r0 + 5]),
+                     fmaxf(s[c][r0 + 6], s[c][r0 + 7]));
+    }
+    float tmax = fmaxf(max3f(pm[0], pm[1], pm[2]), max3f(pm[3], pm[4], max3f(pm[5], pm[6], pm[7])));
     {
       // other lane half (keys of the other 32-row halves): v_permlane32_swap
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
@@ -442,7 +457,7 @@ bsa_fp8_prefill_kernel(Params p) {
     m_run = m_new;
 
     v8i pk[2];
-    float lsum = 0.0f;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -452,7 +467,7 @@ bsa_fp8_prefill_kernel(Params p) {
         const float e1 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 1], cscale, bias));
         const float e2 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 2], cscale, bias));
         const float e3 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 3], cscale, bias));
-        lsum += (e0 + e1) + (e2 + e3);
+        ls[r >> 2] += (e0 + e1) + (e2 + e3);
         // bytes (c&1)*16 + r .. +3 of the P operand of PV step c>>1
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
@@ -466,7 +481,7 @@ bsa_fp8_prefill_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
     }
-    l_run += lsum;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // ---- O^T += V^T . P^T ----------------------------------------------------
     // Transposing read: in each 16-lane group, source lane 2k+q addresses key
@@ -582,6 +597,7 @@ int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache, const
       d.max_seqlen_q < 0 || d.num_heads_q <= 0 || d.num_heads_kv <= 0)
     return BSA_ERR_SIZE;
   if (d.num_heads_q % d.num_heads_kv != 0) return BSA_ERR_GQA;
+  if (d.num_heads_kv > 65536) return BSA_ERR_TOO_LARGE;  // page offsets are 32-bit
   const int group = d.num_heads_q / d.num_heads_kv;
   if (group < 1 || group > 16) return BSA_ERR_GQA;
   {
@@ -632,7 +648,10 @@ int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache, const
   p.mt_grid = mt_grid;
   p.layout = d.kv_layout;
   p.causal = d.causal;
-  p.qk_scale = d.softmax_scale * kLog2e * kF16Widen;
+  p.qk_scale = d.softmax_scale * kLog2e;
+  p.page_bytes = (uint32_t)page_size * (uint32_t)d.num_heads_kv * kHeadDim;
+  p.slot_stride = d.kv_layout == BSA_KV_NHD ? d.num_heads_kv : 1;
+  p.head_stride = d.kv_layout == BSA_KV_NHD ? 1 : page_size;
 
   if (quant_type == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR)
     hipLaunchKernelGGL(bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR>,
