@@ -273,11 +273,15 @@ bsa_fp8_prefill_kernel(Params p) {
   struct PageSet {
     int k, v, ks;
   };
+  // (vzero keeps the V page lookup a per-lane load: a wave-uniform one is moved
+  // to a scalar register at once, which waits for every load in flight)
+  int vzero = 0;
+  asm volatile("" : "+v"(vzero));
   // K row staged by this thread: (wave & 1) * 64 + lane.
   auto lookup = [&](int n, int ln) -> PageSet {
     PageSet ps;
     ps.k = bt[min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) >> p.page_shift];
-    ps.v = bt[min(n * kTile + wave * 32, lkv - 1) >> p.page_shift];
+    ps.v = bt[min(n * kTile + wave * 32 + vzero, lkv - 1) >> p.page_shift];
     ps.ks = QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD
                 ? bt[min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) >> p.page_shift]
                 : 0;
