@@ -41,6 +41,20 @@ the probabilities of a tile, taken against the running maximum after that
 tile, are multiplied by 256 and rounded to E4M3; the row sum uses the
 unrounded probabilities; the final output divides by 256 once and applies the
 V descale.  The output accumulation itself is done in float64.
+
+Two input forms select the sparse KV tiles of a Q tile:
+  * the uint8 block mask [B,Hq,Mt,Kb] (hpc-ops article), tiles visited in
+    ascending order;
+  * the index form of "Quant Block Sparse Attention" ("Key parameters",
+    "Sparse indices & PA page table"): sparse_indices [B,Hq,Mt,Kb] int32 lists
+    logical KV tiles, of which the first sparse_seq_len[b,h,m] are valid.  The
+    set of listed tiles is the sparse set; the emulating mode visits them in
+    list order.  Entries outside [0, ceil(Lkv/128)) select nothing.
+The probability scale of the emulating mode is p_scale ("Key parameters":
+p_scale, a positive finite probability quantisation scale), 256 when not
+given.  Q may come in the TND layout [T,Hq,128] with q_descale [T,Hq] or in the
+NTD layout [Hq,T,128] with q_descale [Hq,T] ("Key parameters": query and
+q_descale layouts); the output is TND either way.
 """
 import numpy as np
 
@@ -52,6 +66,11 @@ NEG_FLT_MAX = -3.4028234663852886e38   # -FLT_MAX, the LSE of an empty sparse se
 
 NHD = 0   # kcache/vcache [num_pages, page_size, Hkv, 128]
 HND = 1   # kcache/vcache [num_pages, Hkv, page_size, 128]
+
+TND = 0   # q [T, Hq, 128], qscale [T, Hq]
+NTD = 1   # q [Hq, T, 128], qscale [Hq, T]
+
+DEFAULT_P_SCALE = 256.0
 
 
 def _ceil_div(a, b):
@@ -91,16 +110,26 @@ def _sequence_bounds(cu_seqlens_q, seqlens_kv, b):
     return t0, lq, lkv
 
 
-def _tile_keys(block_mask, b, h, m, lkv):
-    """Sorted key positions (< lkv) of the KV tiles switched on for Q tile m."""
+def _listed_tiles(sparse_indices, sparse_seq_len, b, h, m, n_tiles):
+    """Valid entries of the index list of Q tile m, in list order."""
+    length = int(sparse_seq_len[b, h, m])
+    entries = np.asarray(sparse_indices[b, h, m, :max(length, 0)], dtype=np.int64)
+    return entries[(entries >= 0) & (entries < n_tiles)]
+
+
+def _tile_keys(block_mask, b, h, m, lkv, index_form=None):
+    """KV tiles selected for Q tile m (in visiting order) and their key
+    positions (< lkv), tile by tile."""
     n_tiles = _ceil_div(lkv, TILE)
-    if block_mask is None:
-        on = np.ones(n_tiles, dtype=bool)     # no mask: the dense path, every tile
+    if index_form is not None:
+        tiles = _listed_tiles(index_form[0], index_form[1], b, h, m, n_tiles)
+    elif block_mask is None:
+        tiles = np.arange(n_tiles)             # no mask: the dense path, every tile
     else:
         row = np.asarray(block_mask[b, h, m, :n_tiles])
         on = np.zeros(n_tiles, dtype=bool)
         on[: row.shape[0]] = row != 0
-    tiles = np.nonzero(on)[0]
+        tiles = np.nonzero(on)[0]
     if tiles.size == 0:
         return tiles, np.zeros(0, dtype=np.int64)
     keys = (tiles[:, None] * TILE + np.arange(TILE)[None, :]).reshape(-1)
@@ -113,7 +142,7 @@ def _q_tile(inp, b, h, m, mode, kcache_deq, vcache_deq):
     rows = np.arange(TILE * m, min(TILE * m + TILE, lq))
     q = e4m3.decode(inp["q"][t0 + rows, h, :]) * \
         np.asarray(inp["qscale"][t0 + rows, h], dtype=np.float64)[:, None]
-    tiles, keys = _tile_keys(inp["block_mask"], b, h, m, lkv)
+    tiles, keys = _tile_keys(inp["block_mask"], b, h, m, lkv, inp["index_form"])
     khat = kcache_deq[keys]
     vhat = vcache_deq[keys]
     scores = inp["softmax_scale"] * (q @ khat.T)                     # [rows, keys]
@@ -134,7 +163,7 @@ def _q_tile(inp, b, h, m, mode, kcache_deq, vcache_deq):
         lse[nonempty] = mx[nonempty] + np.log(lsum[nonempty])
         return rows, o, lse
 
-    # P-emulating mode: ascending active tiles, 128 keys each, online softmax.
+    # P-emulating mode: active tiles in visiting order, 128 keys each, online softmax.
     vcodes = inp["_vcodes_cache"][keys]                               # V^fp8 values (no descale)
     run_max = np.full(rows.size, -np.inf)
     run_sum = np.zeros(rows.size)
@@ -149,19 +178,20 @@ def _q_tile(inp, b, h, m, mode, kcache_deq, vcache_deq):
         safe_new = np.where(np.isfinite(new_max), new_max, 0.0)        # all keys so far masked
         alpha = np.where(np.isfinite(run_max), np.exp(run_max - safe_new), 0.0)
         p_tilde = np.exp(s - safe_new[:, None])                        # masked -> 0
-        p8 = e4m3.round_to_grid(256.0 * p_tilde)                       # fixed P-scale, then E4M3
+        p8 = e4m3.round_to_grid(inp["p_scale"] * p_tilde)              # P-scale, then E4M3
         run_sum = alpha * run_sum + p_tilde.sum(axis=1)
         acc = alpha[:, None] * acc + p8 @ vcodes[cols]
         run_max = new_max
     vs = inp["_vscale_g"]
-    o[nonempty] = acc[nonempty] * vs / (256.0 * run_sum[nonempty, None])
+    o[nonempty] = acc[nonempty] * vs / (inp["p_scale"] * run_sum[nonempty, None])
     lse[nonempty] = run_max[nonempty] + np.log(run_sum[nonempty])
     return rows, o, lse
 
 
 def prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
             seqlens_kv, block_mask, quant_type, page_size, kv_layout=NHD,
-            softmax_scale=None, causal=True, mode="exact", tiles=None):
+            softmax_scale=None, causal=True, mode="exact", tiles=None,
+            sparse_indices=None, sparse_seq_len=None, p_scale=None, q_layout=TND):
     """Oracle of the whole prefill.
 
     Arrays are NumPy: q uint8 [T,Hq,128] (E4M3 codes); kcache/vcache uint8
@@ -170,14 +200,24 @@ def prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table
     [Hkv] (quant 1); cu_seqlens_q int32 [B+1]; block_table int32 [B,pages];
     seqlens_kv int32 [B]; block_mask uint8 [B,Hq,Mt,Kb] or None.
 
-    mode: "exact" (the formula in float64) or "emulate" (fixed P-scale 256
-    with E4M3 rounding of P, see the module docstring).
+    mode: "exact" (the formula in float64) or "emulate" (P-scale, 256 unless
+    p_scale is given, with E4M3 rounding of P, see the module docstring).
     tiles: optional iterable of (b, h, m) Q tiles to compute; every other
     output element is left NaN.  Default: every Q tile of every sequence.
+    sparse_indices / sparse_seq_len: the index form (block_mask must be None).
+    q_layout: TND or NTD for q and qscale.
 
     Returns (O float64 [T,Hq,128], LSE float64 [Hq,T]).
     """
     q = np.asarray(q)
+    qscale = np.asarray(qscale)
+    if q_layout == NTD:                      # [Hq,T,128] and [Hq,T]: same values, axes swapped
+        q = q.transpose(1, 0, 2)
+        qscale = qscale.T
+    index_form = None
+    if sparse_indices is not None:
+        assert block_mask is None, "give either the block mask or the index form"
+        index_form = (np.asarray(sparse_indices), np.asarray(sparse_seq_len))
     T, Hq, D = q.shape
     assert D == HEAD_DIM
     Hkv = kcache.shape[2] if kv_layout == NHD else kcache.shape[1]
@@ -186,9 +226,10 @@ def prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table
     if softmax_scale is None:
         softmax_scale = 1.0 / np.sqrt(HEAD_DIM)
     B = len(seqlens_kv)
-    inp = dict(q=q, qscale=np.asarray(qscale), cu_seqlens_q=np.asarray(cu_seqlens_q),
+    inp = dict(q=q, qscale=qscale, cu_seqlens_q=np.asarray(cu_seqlens_q),
                seqlens_kv=np.asarray(seqlens_kv), block_mask=block_mask,
-               softmax_scale=float(softmax_scale), causal=bool(causal))
+               softmax_scale=float(softmax_scale), causal=bool(causal), index_form=index_form,
+               p_scale=float(DEFAULT_P_SCALE if p_scale is None else p_scale))
     out = np.full((T, Hq, HEAD_DIM), np.nan)
     lse = np.full((Hq, T), np.nan)
 
@@ -224,17 +265,28 @@ def prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table
 
 def brute_force(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
                 seqlens_kv, block_mask, quant_type, page_size, kv_layout=NHD,
-                softmax_scale=None, causal=True):
+                softmax_scale=None, causal=True, sparse_indices=None, sparse_seq_len=None,
+                q_layout=TND):
     """Full-matrix reference for tiny shapes: every (query, key) pair is scored
     and masked element by element, then a plain softmax is taken per row.
 
     The KV sequence is first unpacked from the paged cache into a dense
     [Lkv, Hkv, 128] array by walking the page table slot by slot, and the mask
     decision for pair (t, j) is made from the definition of Omega alone:
-    block_mask[b, h, t // 128, j // 128] != 0, j < Lkv, and (causal) j <= p_t.
+    block_mask[b, h, t // 128, j // 128] != 0 (index form: j // 128 is one of
+    the first sparse_seq_len[b, h, t // 128] entries of the list), j < Lkv, and
+    (causal) j <= p_t.  In the NTD layout q[h, t] and qscale[h, t] are read.
     """
     q = np.asarray(q)
-    T, Hq, D = q.shape
+    if q_layout == NTD:
+        def q_at(t, h):
+            return q[h, t], qscale[h, t]
+        T = q.shape[1]
+    else:
+        def q_at(t, h):
+            return q[t, h], qscale[t, h]
+        T = q.shape[0]
+    Hq, D = (q.shape[0], q.shape[2]) if q_layout == NTD else (q.shape[1], q.shape[2])
     Hkv = kcache.shape[2] if kv_layout == NHD else kcache.shape[1]
     group = Hq // Hkv
     if softmax_scale is None:
@@ -265,11 +317,16 @@ def brute_force(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_t
         for h in range(Hq):
             g = h // group
             for t in range(lq):
-                qv = e4m3.decode(q[t0 + t, h]) * float(qscale[t0 + t, h])
+                qc, qs = q_at(t0 + t, h)
+                qv = e4m3.decode(qc) * float(qs)
                 p = lkv - lq + t
                 allowed = np.zeros(lkv, dtype=bool)
                 for j in range(lkv):
-                    on = True if block_mask is None else block_mask[b, h, t // TILE, j // TILE] != 0
+                    if sparse_indices is not None:
+                        n_valid = int(sparse_seq_len[b, h, t // TILE])
+                        on = any(int(sparse_indices[b, h, t // TILE, k]) == j // TILE for k in range(n_valid))
+                    else:
+                        on = True if block_mask is None else block_mask[b, h, t // TILE, j // TILE] != 0
                     allowed[j] = on and ((not causal) or j <= p)
                 if not allowed.any():
                     out[t0 + t, h] = 0.0

@@ -269,3 +269,43 @@ def sample_q_tiles(problem, count, seed=0, must_include=()):
     chosen = {all_tiles[i] for i in pick}
     chosen.update(tuple(t) for t in must_include)
     return sorted(chosen)
+
+
+def index_form(problem, order="ascending", seed=0, junk=True):
+    """The block mask of `problem` rewritten as per-Q-tile index lists (the index
+    form of "Quant Block Sparse Attention", "Key parameters"): returns
+    (sparse_indices int32 [B,Hq,Mt,Kb+2], sparse_seq_len int32 [B,Hq,Mt]).
+
+    Every non-zero mask entry of a Q tile is listed once.  order: "ascending"
+    or "shuffled" (seeded).  junk: also list two tiles that select nothing
+    (-1 and a tile past the KV length) at seeded positions, and fill the
+    unused tail of every list with arbitrary tile ids (which must be ignored).
+    No arithmetic of the method happens here.
+    """
+    bm = problem.block_mask
+    assert bm is not None
+    B, Hq, Mt, Kb = bm.shape
+    cap = Kb + 2
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(-5, Kb + 5, size=(B, Hq, Mt, cap)).astype(np.int32)   # arbitrary tail
+    seq_len = np.zeros((B, Hq, Mt), dtype=np.int32)
+    for b in range(B):
+        n_tiles = int((problem.seqlens_kv[b] + TILE - 1) // TILE)
+        for h in range(Hq):
+            for m in range(Mt):
+                tiles = np.nonzero(bm[b, h, m])[0].astype(np.int32)
+                if order == "shuffled":
+                    tiles = rng.permutation(tiles)
+                lst = list(tiles)
+                if junk:
+                    for bad in (-1, n_tiles + int(rng.integers(0, 3))):
+                        lst.insert(int(rng.integers(0, len(lst) + 1)), bad)
+                idx[b, h, m, :len(lst)] = lst
+                seq_len[b, h, m] = len(lst)
+    return idx, seq_len
+
+
+def to_ntd(problem):
+    """Q codes and Q descales in the NTD layout: [Hq,T,128] and [Hq,T]."""
+    return (np.ascontiguousarray(problem.q.transpose(1, 0, 2)),
+            np.ascontiguousarray(problem.qscale.T))
