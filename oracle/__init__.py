@@ -16,9 +16,10 @@ Sources (cited by page title and section throughout):
 Contents
   e4m3      -- OCP FP8 E4M3FN codec written from the format definition.
   attention -- exact fp64 oracle, P-emulating oracle, brute-force oracle.
+  schedule  -- task costs and the task order of the scheduling pre-pass.
 
 Every function is pinned by `tests/test_oracle_*.py`; the one part with no
 independent pin ("parity unpinned") is agreement with the pages' own
 implementations, whose outputs the pages do not print.
 """
-from . import e4m3, attention  # noqa: F401
+from . import e4m3, attention, schedule  # noqa: F401
