@@ -14,8 +14,14 @@ hands out tasks as cores free up:
     key some query of the Q tile may attend to (key below Lkv and, in causal
     mode, at or below the query's bottom-right position), 0 for a Q tile that
     starts at or beyond Lq;
-  * order = all task ids by decreasing min(cost, 1023), equal values by
-    increasing id.
+  * the GPU hands workgroup i to XCD i mod 8 (eight XCDs, each with its own
+    L2), so position i of the order runs on XCD i mod 8.  When Hq is a multiple
+    of 8, XCD x is given the contiguous q-head range [x*Hq/8, (x+1)*Hq/8) (all
+    its sequences and Q tiles, so the eight shares have the same shape and the
+    K/V of a kv-head stays within one or two XCDs); its tasks are sorted by
+    decreasing min(cost, 1023), equal values by increasing id, and its j-th
+    task takes position 8j + x.  Otherwise all tasks form one list, sorted the
+    same way, and the j-th task takes position j.
 
 The selection of KV tiles is the one of the attention oracle: mask bytes
 (tiles beyond the mask width are off), or the valid entries of an index list,
@@ -74,7 +80,22 @@ def task_costs(cu_seqlens_q, seqlens_kv, num_heads_q, max_seqlen_q, causal=True,
     return cost
 
 
-def schedule(costs):
-    """Task ids by decreasing min(cost, COST_CAP), ties by increasing id."""
+XCDS = 8
+
+
+def schedule(costs, num_heads_q, max_seqlen_q):
+    """Task id at every launch position (see the module docstring)."""
     c = np.minimum(np.asarray(costs, dtype=np.int64), COST_CAP)
-    return np.lexsort((np.arange(c.size), -c)).astype(np.int32)
+    n = c.size
+    ids = np.arange(n)
+    if num_heads_q % XCDS != 0:
+        return np.lexsort((ids, -c)).astype(np.int32)
+    mt = _ceil_div(int(max_seqlen_q), TILE)
+    head = (ids // mt) % num_heads_q
+    share = head // (num_heads_q // XCDS)             # the XCD that owns the head
+    order = np.lexsort((ids, -c, share))              # share-major, then cost, then id
+    per = n // XCDS
+    out = np.empty(n, dtype=np.int32)
+    j = np.arange(n)
+    out[(j % per) * XCDS + j // per] = order          # j-th task of share x -> 8j + x
+    return out

@@ -93,7 +93,7 @@ def test_hand_example_aligned():
     # h0: m0 {0} -> 1, m1 {1} -> 1, m2 {0,2} -> 2; h1: m0 {} -> 0, m1 {0,1} -> 2, m2 {0,1,2} -> 3
     c = S.task_costs([0, 384], [384], 2, 384, True, block_mask=HAND_MASK)
     np.testing.assert_array_equal(c, [1, 1, 2, 0, 2, 3])
-    np.testing.assert_array_equal(S.schedule(c), [5, 2, 4, 0, 1, 3])
+    np.testing.assert_array_equal(S.schedule(c, 2, 384), [5, 2, 4, 0, 1, 3])
 
 
 def test_hand_example_offset():
@@ -101,7 +101,7 @@ def test_hand_example_offset():
     # key 211 (KV tile 1) and Q tiles 1 and 2 reach KV tile 2.
     c = S.task_costs([0, 300], [384], 2, 300, True, block_mask=HAND_MASK)
     np.testing.assert_array_equal(c, [2, 2, 2, 1, 2, 3])
-    np.testing.assert_array_equal(S.schedule(c), [5, 0, 1, 2, 4, 3])
+    np.testing.assert_array_equal(S.schedule(c, 2, 300), [5, 0, 1, 2, 4, 3])
 
 
 def test_hand_example_non_causal_and_beyond_lq():
@@ -113,7 +113,7 @@ def test_hand_example_non_causal_and_beyond_lq():
     # b0: rows as in the mask (3 KV tiles): 3,2,2 | 2,2,3 ; b1 (2 KV tiles, h order
     # swapped): h0 = HAND_MASK h1 rows: m0 [0,1] -> 1; h1 = HAND_MASK h0: m0 [1,1] -> 2
     np.testing.assert_array_equal(c, [3, 2, 2, 2, 2, 3, 1, 0, 0, 2, 0, 0])
-    np.testing.assert_array_equal(S.schedule(c), [0, 5, 1, 2, 3, 4, 9, 6, 7, 8, 10, 11])
+    np.testing.assert_array_equal(S.schedule(c, 2, 300), [0, 5, 1, 2, 3, 4, 9, 6, 7, 8, 10, 11])
 
 
 def test_index_list_hand_example():
@@ -126,19 +126,19 @@ def test_index_list_hand_example():
     # h0: m0 {2,0} -> tile 0 -> 1; m1 {1} -> 1; m2 {2,0} -> 2
     # h1: m0 {1,2} -> 0; m1 {} -> 0; m2 {1,2,0} -> 3
     np.testing.assert_array_equal(c, [1, 1, 2, 0, 0, 3])
-    np.testing.assert_array_equal(S.schedule(c), [5, 2, 0, 1, 3, 4])
+    np.testing.assert_array_equal(S.schedule(c, 2, 384), [5, 2, 0, 1, 3, 4])
 
 
 def test_dense_costs_closed_form():
     # No sparsity argument, Lq = Lkv = 128 * k, causal: Q tile m costs m + 1.
     c = S.task_costs([0, 640], [640], 1, 640, True)
     np.testing.assert_array_equal(c, [1, 2, 3, 4, 5])
-    np.testing.assert_array_equal(S.schedule(c), [4, 3, 2, 1, 0])
+    np.testing.assert_array_equal(S.schedule(c, 1, 640), [4, 3, 2, 1, 0])
 
 
 def test_order_rule_and_cap():
     c = np.array([5, 2000, 1023, 0, 1500, 5, 7])
-    s = S.schedule(c)
+    s = S.schedule(c, 7, 128)          # 7 heads, one Q tile each: a single list
     np.testing.assert_array_equal(s, [1, 2, 4, 6, 0, 5, 3])
     assert s.dtype == np.int32
 
@@ -147,7 +147,7 @@ def test_order_rule_and_cap():
 def test_schedule_is_sorted_permutation(seed):
     rng = np.random.default_rng(seed)
     c = rng.integers(0, 1100, size=3000)
-    s = S.schedule(c)
+    s = S.schedule(c, 3, 128 * 1000)   # 3 heads: a single list
     assert sorted(s.tolist()) == list(range(c.size))
     key = np.minimum(c[s], 1023)
     assert np.all(np.diff(key) <= 0)
@@ -164,3 +164,32 @@ def test_reach_on_a_tile_boundary():
     # one key short of the boundary: Lkv = 256 puts the last query at 127
     c = S.task_costs([0, 256], [256], 1, 256, True)
     np.testing.assert_array_equal(c, [1, 2])
+
+
+def test_xcd_shares_hand_example():
+    # Hq = 8, one sequence of 2 Q tiles: task id = 2h + m; head h belongs to
+    # XCD h.  Costs (h, m) and the order they give: h0 (1, 3) [1, 0];
+    # h1 (2, 2) [2, 3] (tie: ids); h2 (0, 5) [5, 4]; h3 (1, 4) [7, 6];
+    # h4 (2, 2) [8, 9]; h5 (9, 9) [10, 11]; h6 (0, 0) [12, 13]; h7 (7, 8) [15, 14].
+    # Position 8j + x holds the j-th task of XCD x.
+    c = np.array([1, 3, 2, 2, 0, 5, 1, 4, 2, 2, 9, 9, 0, 0, 7, 8])
+    s = S.schedule(c, 8, 256)
+    want = np.array([1, 2, 5, 7, 8, 10, 12, 15,      # j = 0 for x = 0..7
+                     0, 3, 4, 6, 9, 11, 13, 14])     # j = 1
+    np.testing.assert_array_equal(s, want)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_xcd_shares_properties(seed):
+    rng = np.random.default_rng(seed)
+    hq, mt, B = 16, 7, 3
+    c = rng.integers(0, 1100, size=B * hq * mt)
+    s = S.schedule(c, hq, mt * 128)
+    assert sorted(s.tolist()) == list(range(c.size))
+    head = (s // mt) % hq
+    for x in range(8):
+        mine = s[x::8]                                      # what XCD x runs, in order
+        assert set(head[x::8].tolist()) == {2 * x, 2 * x + 1}
+        key = np.minimum(c[mine], 1023)
+        assert np.all(np.diff(key) <= 0)
+        assert np.all(np.diff(mine)[np.diff(key) == 0] > 0)
