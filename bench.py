@@ -163,6 +163,12 @@ def main():
     ap.add_argument("--workload", default="sparse16k")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--form", choices=("mask", "list"), default="mask",
+                    help="sparsity argument: the uint8 block mask, or the same tiles as ascending "
+                         "index lists (sparse_indices + sparse_seq_len)")
+    ap.add_argument("--schedule", action="store_true",
+                    help="run the scheduling pre-pass inside every step and launch the prefill "
+                         "in its task order")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="record HBM traffic of --workload from rocprofv3 counter CSV directories and exit")
     ap.add_argument("--ingest-command", default="", help="command line recorded with --ingest-counters")
@@ -198,12 +204,41 @@ def main():
     out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
 
+    si = sl = None
+    if args.form == "list":
+        from synth import index_form
+        idx, slen = index_form(p, "ascending", junk=False)
+        si = torch.from_numpy(idx).cuda()
+        sl = torch.from_numpy(slen).cuda()
+    mask = d["block_mask"] if si is None else None
+    sched = ws = None
+    if args.schedule:
+        ntasks = len(p.seqlens_kv) * Hq * ((p.max_seqlen_q + TILE - 1) // TILE)
+        sched = torch.empty(ntasks, dtype=torch.int32, device="cuda")
+        ws = torch.empty(bsa.bsa_fp8_schedule_workspace_bytes(len(p.seqlens_kv), Hq, p.max_seqlen_q),
+                         dtype=torch.uint8, device="cuda")
+
+    def pre_pass():
+        bsa.bsa_fp8_schedule(d["cu_seqlens_q"], d["seqlens_kv"], mask, num_heads_q=Hq,
+                             max_seqlen_q=p.max_seqlen_q, causal=p.causal, sparse_indices=si,
+                             sparse_seq_len=sl, workspace=ws, schedule=sched)
+
     def step():
-        bsa.bsa_fp8_prefill(d["q"], d["kcache"], d["vcache"], d["qscale"], d["kscale"], d["vscale"],
-                            d["cu_seqlens_q"], d["block_table"], d["seqlens_kv"], d["block_mask"],
-                            p.quant_type, p.page_size, max_seqlen_q=p.max_seqlen_q,
-                            kv_layout=p.kv_layout, causal=p.causal,
-                            softmax_scale=p.softmax_scale, out=out, lse=lse)
+        if args.form == "mask" and not args.schedule:
+            bsa.bsa_fp8_prefill(d["q"], d["kcache"], d["vcache"], d["qscale"], d["kscale"],
+                                d["vscale"], d["cu_seqlens_q"], d["block_table"], d["seqlens_kv"],
+                                d["block_mask"], p.quant_type, p.page_size,
+                                max_seqlen_q=p.max_seqlen_q, kv_layout=p.kv_layout,
+                                causal=p.causal, softmax_scale=p.softmax_scale, out=out, lse=lse)
+            return
+        if args.schedule:
+            pre_pass()
+        bsa.bsa_fp8_prefill_ex(d["q"], d["kcache"], d["vcache"], d["qscale"], d["kscale"],
+                               d["vscale"], d["cu_seqlens_q"], d["block_table"], d["seqlens_kv"],
+                               mask, p.quant_type, p.page_size, max_seqlen_q=p.max_seqlen_q,
+                               kv_layout=p.kv_layout, causal=p.causal,
+                               softmax_scale=p.softmax_scale, sparse_indices=si,
+                               sparse_seq_len=sl, schedule=sched, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -220,6 +255,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    schedule_ms = None
+    if args.schedule:
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for s, e in pe:
+            s.record(stream)
+            pre_pass()
+            e.record(stream)
+        torch.cuda.synchronize()
+        schedule_ms = round(float(np.mean([s.elapsed_time(e) for s, e in pe])), 4)
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
     flop = n_act * FLOP_PER_TILE
     kv_bytes = n_act * (KV_BYTES_PER_TILE + (TILE * 4 if p.quant_type == 1 else 0))
@@ -239,16 +284,19 @@ def main():
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded N(0,1) quantised to E4M3, random paging and block mask)",
         "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "active_tiles": n_act,
-                   "q_tokens": T, "causal": bool(p.causal)},
+                   "q_tokens": T, "causal": bool(p.causal), "sparsity_form": args.form,
+                   "schedule_pre_pass": bool(args.schedule)},
         "tokens_per_s": round(T / (wall / args.steps), 1),
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "useful_tflops": round(pairs * 4 * TILE / (wall / args.steps) / 1e12, 2),
         "kv_gbps_logical": round(kv_bytes / (wall / args.steps) / 1e9, 1),
         "kernel_ms_min": round(float(kernel_ms.min()), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
+        "schedule_pre_pass_ms": schedule_ms,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": recorded_traffic(p.cfg.name)},
+                     "traffic": recorded_traffic(p.cfg.name)
+                     if args.form == "mask" and not args.schedule else None},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, n_act, args.cpu_budget)

@@ -18,7 +18,11 @@ __all__ = [
     "QuantType",
     "KVLayout",
     "BsaError",
+    "QLayout",
     "bsa_fp8_prefill",
+    "bsa_fp8_prefill_ex",
+    "bsa_fp8_schedule",
+    "bsa_fp8_schedule_workspace_bytes",
     "attention_with_kvcache_blocksparse_prefill_fp8",
     "library_path",
     "load_library",
@@ -41,6 +45,12 @@ class QuantType(enum.IntEnum):
 class KVLayout(enum.IntEnum):
     NHD = 0  # [num_pages, page_size, Hkv, 128]
     HND = 1  # [num_pages, Hkv, page_size, 128]
+
+
+class QLayout(enum.IntEnum):
+    """Query layouts ("Quant Block Sparse Attention", "Key parameters")."""
+    TND = 0  # q [T, Hq, 128], qscale [T, Hq]
+    NTD = 1  # q [Hq, T, 128], qscale [Hq, T]
 
 
 class BsaError(RuntimeError):
@@ -70,6 +80,17 @@ class Dims(ctypes.Structure):
 _lib_handle = None
 
 
+class Options(ctypes.Structure):
+    _fields_ = [
+        ("q_layout", ctypes.c_int32),
+        ("p_scale", ctypes.c_float),
+        ("sparse_indices", ctypes.c_void_p),
+        ("sparse_seq_len", ctypes.c_void_p),
+        ("schedule", ctypes.c_void_p),
+        ("schedule_len", ctypes.c_int32),
+    ]
+
+
 def load_library():
     """Load libbsa_fp8.so (once).  Raises RuntimeError if it is not built."""
     global _lib_handle
@@ -85,6 +106,15 @@ def load_library():
     lib.bsa_fp8_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_int, ctypes.c_int, ctypes.POINTER(Dims), vp, vp, vp]
     lib.bsa_fp8_prefill.restype = ctypes.c_int
+    lib.bsa_fp8_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_int, ctypes.c_int, ctypes.POINTER(Dims),
+                                       ctypes.POINTER(Options), vp, vp, vp]
+    lib.bsa_fp8_prefill_ex.restype = ctypes.c_int
+    lib.bsa_fp8_schedule_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+    lib.bsa_fp8_schedule_workspace_bytes.restype = ctypes.c_longlong
+    lib.bsa_fp8_schedule.argtypes = [vp, vp, vp, ctypes.POINTER(Dims), ctypes.POINTER(Options),
+                                     vp, vp, vp]
+    lib.bsa_fp8_schedule.restype = ctypes.c_int
     lib.bsa_fp8_status_string.argtypes = [ctypes.c_int]
     lib.bsa_fp8_status_string.restype = ctypes.c_char_p
     lib.bsa_fp8_abi_version.argtypes = []
@@ -115,18 +145,39 @@ def _check(name, t, dtypes, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def bsa_fp8_prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
-                    seqlens_kv, block_mask, quant_type, page_size, *, max_seqlen_q,
-                    kv_layout=KVLayout.NHD, causal=True, softmax_scale=None,
-                    out=None, lse=None, return_lse=True, stream=None):
-    """Call the C entry point of the same name.  Returns (out, lse).
+def _sparsity_shape(block_mask, sparse_indices, sparse_seq_len, device):
+    """(mask_tiles_q, mask_tiles_kv) of the sparsity argument, after checks."""
+    if block_mask is not None:
+        _check("block_mask", block_mask, (torch.uint8, torch.bool), device)
+        if block_mask.dim() != 4:
+            raise ValueError("block_mask must be [B, Hq, mask_tiles_q, mask_tiles_kv]")
+        return block_mask.shape[2], block_mask.shape[3]
+    if sparse_indices is not None or sparse_seq_len is not None:
+        if sparse_indices is None or sparse_seq_len is None:
+            raise ValueError("sparse_indices and sparse_seq_len come together")
+        _check("sparse_indices", sparse_indices, (torch.int32,), device)
+        _check("sparse_seq_len", sparse_seq_len, (torch.int32,), device)
+        if sparse_indices.dim() != 4 or sparse_seq_len.shape != sparse_indices.shape[:3]:
+            raise ValueError("sparse_indices must be [B, Hq, Qb, Kb] and sparse_seq_len [B, Hq, Qb]")
+        return sparse_indices.shape[2], sparse_indices.shape[3]
+    return 0, 0
 
-    Shapes and meaning are those of ``include/bsa_fp8.h``.  ``out`` (bf16
-    [T,Hq,128]) and ``lse`` (float32 [Hq,T]) are allocated when not given.
-    """
+
+def _options(q_layout, p_scale, sparse_indices, sparse_seq_len, schedule):
+    return Options(q_layout=int(q_layout), p_scale=0.0 if p_scale is None else float(p_scale),
+                   sparse_indices=None if sparse_indices is None else sparse_indices.data_ptr(),
+                   sparse_seq_len=None if sparse_seq_len is None else sparse_seq_len.data_ptr(),
+                   schedule=None if schedule is None else schedule.data_ptr(),
+                   schedule_len=0 if schedule is None else schedule.numel())
+
+
+def _prefill(entry, q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
+             seqlens_kv, block_mask, quant_type, page_size, max_seqlen_q, kv_layout, causal,
+             softmax_scale, out, lse, return_lse, stream, q_layout=QLayout.TND, p_scale=None,
+             sparse_indices=None, sparse_seq_len=None, schedule=None):
     device = q.device
     if device.type != "cuda":
-        raise ValueError("bsa_fp8_prefill runs on a GPU; q is on " + str(device))
+        raise ValueError(entry + " runs on a GPU; q is on " + str(device))
     _check("q", q, _FP8, device)
     _check("kcache", kcache, _FP8, device)
     _check("vcache", vcache, _FP8, device)
@@ -135,13 +186,16 @@ def bsa_fp8_prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, blo
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("block_table", block_table),
                     ("seqlens_kv", seqlens_kv)):
         _check(name, t, (torch.int32,), device)
-    if block_mask is not None:
-        _check("block_mask", block_mask, (torch.uint8, torch.bool), device)
-        if block_mask.dim() != 4:
-            raise ValueError("block_mask must be [B, Hq, mask_tiles_q, mask_tiles_kv]")
+    mt, mkv = _sparsity_shape(block_mask, sparse_indices, sparse_seq_len, device)
+    if schedule is not None:
+        _check("schedule", schedule, (torch.int32,), device)
     if q.dim() != 3 or kcache.dim() != 4 or vcache.shape != kcache.shape:
-        raise ValueError("q must be [T,Hq,D]; kcache/vcache must be 4-D and of equal shape")
-    T, Hq, D = q.shape
+        raise ValueError("q must be 3-D; kcache/vcache must be 4-D and of equal shape")
+    q_layout = QLayout(int(q_layout))
+    if q_layout == QLayout.TND:
+        T, Hq, D = q.shape
+    else:
+        Hq, T, D = q.shape
     kv_layout = KVLayout(int(kv_layout))
     Hkv = kcache.shape[2] if kv_layout == KVLayout.NHD else kcache.shape[1]
     B = seqlens_kv.shape[0]
@@ -157,23 +211,115 @@ def bsa_fp8_prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, blo
         _check("lse", lse, (torch.float32,), device)
     dims = Dims(batch=B, total_q=T, num_heads_q=Hq, num_heads_kv=Hkv, head_dim=D,
                 num_pages=kcache.shape[0], max_pages_per_seq=block_table.shape[1],
-                max_seqlen_q=int(max_seqlen_q),
-                mask_tiles_q=block_mask.shape[2] if block_mask is not None else 0,
-                mask_tiles_kv=block_mask.shape[3] if block_mask is not None else 0,
+                max_seqlen_q=int(max_seqlen_q), mask_tiles_q=mt, mask_tiles_kv=mkv,
                 kv_layout=int(kv_layout), causal=1 if causal else 0,
                 softmax_scale=float(softmax_scale))
     if stream is None:
         stream = torch.cuda.current_stream(device).cuda_stream
     lib = load_library()
     mask_u8 = block_mask.view(torch.uint8) if block_mask is not None else None
-    status = lib.bsa_fp8_prefill(
-        _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(qscale), _ptr(kscale), _ptr(vscale),
-        _ptr(cu_seqlens_q), _ptr(block_table), _ptr(seqlens_kv), _ptr(mask_u8),
-        int(quant_type), int(page_size), ctypes.byref(dims), _ptr(out), _ptr(lse),
-        ctypes.c_void_p(stream))
+    args = [_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(qscale), _ptr(kscale), _ptr(vscale),
+            _ptr(cu_seqlens_q), _ptr(block_table), _ptr(seqlens_kv), _ptr(mask_u8),
+            int(quant_type), int(page_size), ctypes.byref(dims)]
+    if entry == "bsa_fp8_prefill_ex":
+        opts = _options(q_layout, p_scale, sparse_indices, sparse_seq_len, schedule)
+        args.append(ctypes.byref(opts))
+    args += [_ptr(out), _ptr(lse), ctypes.c_void_p(stream)]
+    status = getattr(lib, entry)(*args)
     if status != 0:
         raise BsaError(status, status_string(status))
     return out, lse
+
+
+def bsa_fp8_prefill(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
+                    seqlens_kv, block_mask, quant_type, page_size, *, max_seqlen_q,
+                    kv_layout=KVLayout.NHD, causal=True, softmax_scale=None,
+                    out=None, lse=None, return_lse=True, stream=None):
+    """Call the C entry point of the same name.  Returns (out, lse).
+
+    Shapes and meaning are those of ``include/bsa_fp8.h``.  ``out`` (bf16
+    [T,Hq,128]) and ``lse`` (float32 [Hq,T]) are allocated when not given.
+    """
+    return _prefill("bsa_fp8_prefill", q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q,
+                    block_table, seqlens_kv, block_mask, quant_type, page_size, max_seqlen_q,
+                    kv_layout, causal, softmax_scale, out, lse, return_lse, stream)
+
+
+def bsa_fp8_prefill_ex(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
+                       seqlens_kv, block_mask, quant_type, page_size, *, max_seqlen_q,
+                       kv_layout=KVLayout.NHD, causal=True, softmax_scale=None,
+                       q_layout=QLayout.TND, p_scale=None, sparse_indices=None,
+                       sparse_seq_len=None, schedule=None,
+                       out=None, lse=None, return_lse=True, stream=None):
+    """Call the C entry point of the same name: bsa_fp8_prefill plus the query
+    layout (q [Hq,T,128] and qscale [Hq,T] for NTD), the P-scale (None = 256),
+    the index-list sparsity (sparse_indices int32 [B,Hq,Qb,Kb] with
+    sparse_seq_len int32 [B,Hq,Qb], instead of block_mask) and a task order
+    from ``bsa_fp8_schedule``.  Returns (out, lse); out is TND."""
+    return _prefill("bsa_fp8_prefill_ex", q, kcache, vcache, qscale, kscale, vscale,
+                    cu_seqlens_q, block_table, seqlens_kv, block_mask, quant_type, page_size,
+                    max_seqlen_q, kv_layout, causal, softmax_scale, out, lse, return_lse, stream,
+                    q_layout=q_layout, p_scale=p_scale, sparse_indices=sparse_indices,
+                    sparse_seq_len=sparse_seq_len, schedule=schedule)
+
+
+def _schedule_dims(batch, num_heads_q, max_seqlen_q, mt, mkv, causal):
+    # The pre-pass reads only the sequence lengths and the sparsity; the other
+    # fields take any valid value.
+    return Dims(batch=batch, total_q=0, num_heads_q=num_heads_q, num_heads_kv=num_heads_q,
+                head_dim=128, num_pages=0, max_pages_per_seq=0, max_seqlen_q=int(max_seqlen_q),
+                mask_tiles_q=mt, mask_tiles_kv=mkv, kv_layout=0, causal=1 if causal else 0,
+                softmax_scale=1.0)
+
+
+def bsa_fp8_schedule_workspace_bytes(batch, num_heads_q, max_seqlen_q):
+    """Device workspace (bytes) the scheduling pre-pass needs."""
+    dims = _schedule_dims(batch, num_heads_q, max_seqlen_q, 1, 1, True)
+    n = load_library().bsa_fp8_schedule_workspace_bytes(ctypes.byref(dims))
+    if n < 0:
+        raise ValueError("invalid sizes for the scheduling pre-pass")
+    return n
+
+
+def bsa_fp8_schedule(cu_seqlens_q, seqlens_kv, block_mask=None, *, num_heads_q, max_seqlen_q,
+                     causal=True, sparse_indices=None, sparse_seq_len=None, workspace=None,
+                     schedule=None, stream=None):
+    """Call the C entry point of the same name: the task order (int32
+    [B*Hq*ceil(max_seqlen_q/128)], decreasing cost, then increasing task id) for
+    ``bsa_fp8_prefill_ex``.  The workspace is allocated when not given."""
+    device = seqlens_kv.device
+    if device.type != "cuda":
+        raise ValueError("bsa_fp8_schedule runs on a GPU; seqlens_kv is on " + str(device))
+    _check("cu_seqlens_q", cu_seqlens_q, (torch.int32,), device)
+    _check("seqlens_kv", seqlens_kv, (torch.int32,), device)
+    mt, mkv = _sparsity_shape(block_mask, sparse_indices, sparse_seq_len, device)
+    B = seqlens_kv.shape[0]
+    dims = _schedule_dims(B, num_heads_q, max_seqlen_q, mt, mkv, causal)
+    lib = load_library()
+    nbytes = lib.bsa_fp8_schedule_workspace_bytes(ctypes.byref(dims))
+    if nbytes < 0:
+        raise ValueError("invalid sizes for the scheduling pre-pass")
+    ntasks = B * num_heads_q * ((int(max_seqlen_q) + 127) // 128)
+    if schedule is None:
+        schedule = torch.empty(ntasks, dtype=torch.int32, device=device)
+    else:
+        _check("schedule", schedule, (torch.int32,), device)
+        if schedule.numel() != ntasks:
+            raise ValueError(f"schedule must hold {ntasks} task ids")
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must hold {nbytes} bytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    mask_u8 = block_mask.view(torch.uint8) if block_mask is not None else None
+    opts = _options(QLayout.TND, None, sparse_indices, sparse_seq_len, None)
+    status = lib.bsa_fp8_schedule(_ptr(cu_seqlens_q), _ptr(seqlens_kv), _ptr(mask_u8),
+                                  ctypes.byref(dims), ctypes.byref(opts), _ptr(workspace),
+                                  _ptr(schedule), ctypes.c_void_p(stream))
+    if status != 0:
+        raise BsaError(status, status_string(status))
+    return schedule
 
 
 def attention_with_kvcache_blocksparse_prefill_fp8(

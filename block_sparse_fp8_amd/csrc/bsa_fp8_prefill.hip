@@ -9,7 +9,10 @@
 //      set bits in ascending order, so every wave sees the same ordered list
 //      without a round trip through LDS.  The candidates are clipped to the KV
 //      length and, in causal mode, to the last tile any query of the Q tile can
-//      see.  Tiles the mask switches off are never read.
+//      see.  Tiles the mask switches off are never read.  In the index-list
+//      form the same ballot runs over 64 list entries at a time (valid = a
+//      tile id inside the candidate range) and the tile id is read from the
+//      entry's lane, so tiles are visited in list order.
 //   2. Per active tile, K and V rows are gathered from the paged cache (one
 //      page-table lookup per row).  V (and, for per-token K scales, the K
 //      descales) go straight to LDS with direct-to-LDS loads, double-buffered;
@@ -26,17 +29,19 @@
 //      64-key half of the tile, in register order.
 //   4. Online softmax in fp32 in the log2 domain: qscale*softmax_scale*log2(e)
 //      (and the per-tensor K descale, and 2^16 for the f16 widening) is one
-//      per-lane constant; P' = exp2(x - m + 8) = 256*exp(score - max), i.e. the
-//      fixed P-scale of 256 (hpc-ops article, "FP8 Tensor Core compute: fixed
-//      P-scale quantisation") costs nothing.  P' is rounded to E4M3
+//      per-lane constant; P' = exp2(x - m + log2(p_scale)) = p_scale*exp(score
+//      - max), so the P-scale (256 by default: hpc-ops article, "FP8 Tensor
+//      Core compute: fixed P-scale quantisation"; any p_scale in (0, 448]:
+//      "Quant Block Sparse Attention", "Key parameters") costs nothing.  P' is
+//      rounded to E4M3
 //      (v_cvt_pk_fp8_f32, round to nearest even) and the row sum keeps the
 //      unrounded P'.  The accumulator rescale is skipped when no row of the
 //      wave has a new maximum (the factor is then exactly 1).
 //   5. O^T += V^T . P^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3).  V stays
 //      row-major in LDS; the transposing read ds_read_b64_tr_b8 delivers it
 //      key-major.
-//   6. Epilogue: O = O_acc * vdescale / sum(P') (the 1/256 is inside the sum),
-//      written as bf16; LSE = ln2 * (m + log2(sum) - 8).  A query whose sparse
+//   6. Epilogue: O = O_acc * vdescale / sum(P') (the 1/p_scale is inside the
+//      sum), written as bf16; LSE = ln2 * (m + log2(sum) - log2(p_scale)).  A query whose sparse
 //      set is empty gets O = 0 and LSE = -FLT_MAX ("Quant Block Sparse
 //      Attention", "Sparse indices & PA page table").
 
@@ -47,16 +52,18 @@
 #include <string.h>
 
 #include "bsa_fp8.h"
+#include "bsa_internal.h"
 
 namespace {
 
-constexpr int kTile = 128;
-constexpr int kHeadDim = 128;
+using bsa::kTile;
+using bsa::kHeadDim;
+using bsa::kFormList;
+using bsa::candidate_end;
 constexpr int kThreads = 256;
 constexpr int kK16Row = 2 * kHeadDim;  // bytes per f16 K row in LDS
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kPScaleLog2 = 8.0f;      // P is scaled by 2^8 = 256 before rounding to E4M3
 constexpr float kNegFltMax = -3.402823466e+38f;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -80,6 +87,9 @@ struct Params {
   const int32_t* block_table;
   const int32_t* seqlens_kv;
   const uint8_t* mask;
+  const int32_t* sidx;      // index-list form: [B, Hq, mt, mkv] tile ids
+  const int32_t* slen;      // index-list form: [B, Hq, mt] valid lengths
+  const int32_t* schedule;  // task order, or nullptr for the built-in order
   uint16_t* out;
   float* lse;
   int B, T, Hq, Hkv, group;
@@ -87,6 +97,9 @@ struct Params {
   int mt, mkv, mt_grid;
   int layout, causal;
   float qk_scale;       // softmax_scale * log2(e)
+  float pscale_log2;    // log2(p_scale)
+  int q_tok_stride;     // q rows (of 128 B) between consecutive tokens: Hq (TND) or 1 (NTD)
+  int q_head_stride;    // q rows between consecutive heads: 1 (TND) or T (NTD)
   uint32_t page_bytes;  // bytes of one page of K (or V) cache: page_size * Hkv * 128
   int slot_stride;      // rows between consecutive slots of a page (Hkv for NHD, 1 for HND)
   int head_stride;      // rows between consecutive kv-heads of a page (1 for NHD, page_size for HND)
@@ -122,7 +135,7 @@ __device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // Wave-uniform walk over the active KV tiles of one Q tile, in ascending order.
-struct TileWalk {
+struct MaskWalk {
   const uint8_t* row;  // mask row, or nullptr for the dense path
   int n_end;           // candidates are 0 .. n_end-1
   int base;            // first candidate of the current 64-tile chunk
@@ -153,7 +166,42 @@ struct TileWalk {
   }
 };
 
-template <int QUANT>
+// Wave-uniform walk over an index list, in list order.  Entries outside
+// [0, n_end) select no key any query of the Q tile may see and are skipped.
+struct ListWalk {
+  const int32_t* row;  // the Q tile's list
+  int len;             // valid entries: 0 .. len-1
+  int n_end;           // candidate tiles are 0 .. n_end-1
+  int base;            // first entry of the current 64-entry chunk
+  uint64_t bits;       // usable entries of the chunk not yet returned
+  int ent;             // this lane's entry of the chunk
+
+  __device__ void init(const int32_t* r, int length, int end, int lane) {
+    row = r;
+    len = length;
+    n_end = end;
+    base = 0;
+    bits = len > 0 ? load_chunk(lane) : 0;
+  }
+  __device__ uint64_t load_chunk(int lane) {
+    int i = base + lane;
+    asm volatile("" : "+v"(i));
+    ent = i < len ? row[i] : -1;
+    return __ballot(ent >= 0 && ent < n_end);
+  }
+  __device__ int next(int lane) {
+    while (bits == 0) {
+      base += 64;
+      if (base >= len) return -1;
+      bits = load_chunk(lane);
+    }
+    const int pos = (int)__builtin_ctzll(bits);
+    bits &= bits - 1;
+    return __builtin_amdgcn_readlane(ent, pos);
+  }
+};
+
+template <int QUANT, int FORM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bsa_fp8_prefill_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t k16_lds[kTile * kK16Row];       // 32 KB
@@ -167,21 +215,49 @@ bsa_fp8_prefill_kernel(Params p) {
   const int col = lane & 31;  // query column owned by this lane within the wave
 
   // Work order.  The hardware hands consecutive workgroup ids to the 8 XCDs
-  // round-robin; id i is remapped so that XCD (i % 8) walks a contiguous slice
-  // of the logical list, which is ordered by kv-group (kv-head outer, sequence
-  // inner), then Q tile from the last (most causal work) down, then q-head
-  // within the group.  Each XCD's L2 then serves the K/V of its own kv-heads.
+  // round-robin.  Without a schedule, id i is remapped so that XCD (i % 8)
+  // walks its own share of the tasks (below); when Hq is not a multiple of 8
+  // the share is a contiguous slice of the list ordered by kv-group (kv-head
+  // outer, sequence inner), then Q tile from the last down, then q-head within
+  // the group.  Each XCD's L2 then serves the K/V of its own kv-heads.
+  // A schedule (from the pre-pass) names the task directly: task id
+  // (b * Hq + h) * mt_grid + m.
   const int total = p.B * p.Hq * p.mt_grid;
-  const int per_xcd = total >> 3;
-  const int i = (int)blockIdx.x;
-  const int L = i < (per_xcd << 3) ? (i & 7) * per_xcd + (i >> 3) : i;
-  const int per_group = p.group * p.mt_grid;
-  const int gi = L / per_group;
-  const int within = L - gi * per_group;
-  const int m = p.mt_grid - 1 - within / p.group;
-  const int b = gi % p.B;
-  const int g = gi / p.B;
-  const int h = g * p.group + within % p.group;
+  int m, b, h, g;
+  if (p.schedule != nullptr) {
+    const int task = p.schedule[blockIdx.x];
+    if ((unsigned)task >= (unsigned)total) return;  // not a task id: nothing to do
+    m = task % p.mt_grid;
+    const int bh = task / p.mt_grid;
+    h = bh % p.Hq;
+    b = bh / p.Hq;
+    g = h / p.group;
+  } else if ((p.Hq & 7) == 0) {
+    // Workgroup i runs on XCD i % 8.  XCD x owns q-heads [x*Hq/8, (x+1)*Hq/8),
+    // every sequence and Q tile of them, so the eight shares have the same
+    // shape and a kv-head's K/V stays within one or two XCDs' L2.  Within a
+    // share: sequence, then Q tile from the last (most causal work) down, then
+    // head.
+    const int x = (int)(blockIdx.x & 7);
+    const int r = (int)(blockIdx.x >> 3);
+    const int hpx = p.Hq >> 3;
+    const int q = r / hpx;
+    h = x * hpx + (r - q * hpx);
+    m = p.mt_grid - 1 - q % p.mt_grid;
+    b = q / p.mt_grid;
+    g = h / p.group;
+  } else {
+    const int per_xcd = total >> 3;
+    const int i = (int)blockIdx.x;
+    const int L = i < (per_xcd << 3) ? (i & 7) * per_xcd + (i >> 3) : i;
+    const int per_group = p.group * p.mt_grid;
+    const int gi = L / per_group;
+    const int within = L - gi * per_group;
+    m = p.mt_grid - 1 - within / p.group;
+    b = gi % p.B;
+    g = gi / p.B;
+    h = g * p.group + within % p.group;
+  }
 
   const int t0 = p.cu_q[b];
   const int lq = p.cu_q[b + 1] - t0;
@@ -189,19 +265,21 @@ bsa_fp8_prefill_kernel(Params p) {
   if (m * kTile >= lq) return;  // Q tile beyond this sequence (uniform per workgroup)
 
   // Candidate KV tiles: below the KV length, within the causal range of some
-  // query of this Q tile, and within the mask width.
-  int n_end = (lkv + kTile - 1) / kTile;
-  if (p.causal) {
-    const int p_max = lkv - lq + min(m * kTile + kTile - 1, lq - 1);
-    n_end = p_max >= 0 ? min(n_end, p_max / kTile + 1) : 0;
+  // query of this Q tile, and (mask form) within the mask width.
+  int n_end = candidate_end(lq, lkv, m, p.causal);
+  const int64_t qrow = ((int64_t)b * p.Hq + h) * p.mt + m;  // row of the sparsity arrays
+  std::conditional_t<FORM == kFormList, ListWalk, MaskWalk> walk;
+  if constexpr (FORM == kFormList) {
+    const int len = min(max(p.slen[qrow], 0), p.mkv);
+    walk.init(p.sidx + qrow * p.mkv, len, n_end, lane);
+  } else {
+    const uint8_t* mask_row = nullptr;
+    if (p.mask != nullptr) {
+      n_end = min(n_end, p.mkv);
+      mask_row = p.mask + qrow * p.mkv;
+    }
+    walk.init(mask_row, n_end, lane);
   }
-  const uint8_t* mask_row = nullptr;
-  if (p.mask != nullptr) {
-    n_end = min(n_end, p.mkv);
-    mask_row = p.mask + (((int64_t)b * p.Hq + h) * p.mt + m) * p.mkv;
-  }
-  TileWalk walk;
-  walk.init(mask_row, n_end, lane);
 
   // Queries of this lane.
   const int tq = m * kTile + wave * 32 + col;             // query index within the sequence
@@ -215,10 +293,11 @@ bsa_fp8_prefill_kernel(Params p) {
   {
     v2i raw[8];
     if (q_valid) {
-      const uint8_t* qp = p.q + ((int64_t)(t0 + tq) * p.Hq + h) * kHeadDim + hd * 8;
+      const int64_t qi = (int64_t)(t0 + tq) * p.q_tok_stride + (int64_t)h * p.q_head_stride;
+      const uint8_t* qp = p.q + qi * kHeadDim + hd * 8;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) raw[ks] = *reinterpret_cast<const v2i*>(qp + ks * 16);
-      cscale = p.qscale[(int64_t)(t0 + tq) * p.Hq + h] * p.qk_scale;
+      cscale = p.qscale[qi] * p.qk_scale;
     } else {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) raw[ks] = v2i{0, 0};
@@ -456,7 +535,7 @@ bsa_fp8_prefill_kernel(Params p) {
     const float m_new = fmaxf(m_run, tmax_x);
     const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);  // exp2(-inf) = 0
-    const float bias = kPScaleLog2 - m_safe;
+    const float bias = p.pscale_log2 - m_safe;
     const bool rescale = __ballot(m_new != m_run) != 0;
     m_run = m_new;
 
@@ -555,7 +634,7 @@ bsa_fp8_prefill_kernel(Params p) {
     }
   }
   if (p.lse != nullptr && hd == 0) {
-    p.lse[(int64_t)h * p.T + t0 + tq] = empty ? kNegFltMax : (m_run + log2f(l_tot) - kPScaleLog2) * kLn2;
+    p.lse[(int64_t)h * p.T + t0 + tq] = empty ? kNegFltMax : (m_run + log2f(l_tot) - p.pscale_log2) * kLn2;
   }
 }
 
@@ -563,7 +642,7 @@ bsa_fp8_prefill_kernel(Params p) {
 
 extern "C" {
 
-int bsa_fp8_abi_version(void) { return 1; }
+int bsa_fp8_abi_version(void) { return 2; }
 
 const char* bsa_fp8_status_string(int status) {
   switch (status) {
@@ -579,45 +658,29 @@ const char* bsa_fp8_status_string(int status) {
     case BSA_ERR_SOFTMAX_SCALE: return "softmax_scale must be finite";
     case BSA_ERR_TOO_LARGE: return "problem exceeds a supported limit";
     case BSA_ERR_LAUNCH: return "kernel launch failed";
+    case BSA_ERR_Q_LAYOUT: return "unknown q_layout";
+    case BSA_ERR_P_SCALE: return "p_scale must be 0 (default 256) or in (0, 448]";
+    case BSA_ERR_SPARSE_FORM: return "give block_mask or sparse_indices with sparse_seq_len, not both";
+    case BSA_ERR_SCHEDULE: return "schedule_len must equal the task count";
     default: return "unknown status";
   }
 }
 
-int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache, const float* qscale,
-                    const float* kscale, const float* vscale, const int32_t* cu_seqlens_q,
-                    const int32_t* block_table, const int32_t* seqlens_kv, const uint8_t* block_mask,
-                    int quant_type, int page_size, const bsa_fp8_dims* dims, void* out, float* lse,
-                    void* stream) {
+int bsa_fp8_prefill_ex(const void* q, const void* kcache, const void* vcache, const float* qscale,
+                       const float* kscale, const float* vscale, const int32_t* cu_seqlens_q,
+                       const int32_t* block_table, const int32_t* seqlens_kv, const uint8_t* block_mask,
+                       int quant_type, int page_size, const bsa_fp8_dims* dims,
+                       const bsa_fp8_options* options, void* out, float* lse, void* stream) {
   // ---- static validation (host only, before any HIP call) ----
-  if (dims == nullptr) return BSA_ERR_NULL_POINTER;
-  const bsa_fp8_dims d = *dims;
-  if (d.head_dim != kHeadDim) return BSA_ERR_HEAD_DIM;
+  bsa::Resolved r;
+  const int st = bsa::resolve(dims, block_mask, options, &r);
+  if (st != BSA_OK) return st;
   if (page_size != 32 && page_size != 64) return BSA_ERR_PAGE_SIZE;
   if (quant_type != BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR &&
       quant_type != BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD)
     return BSA_ERR_QUANT_TYPE;
-  if (d.kv_layout != BSA_KV_NHD && d.kv_layout != BSA_KV_HND) return BSA_ERR_KV_LAYOUT;
-  if (d.batch < 0 || d.total_q < 0 || d.num_pages < 0 || d.max_pages_per_seq < 0 ||
-      d.max_seqlen_q < 0 || d.num_heads_q <= 0 || d.num_heads_kv <= 0)
-    return BSA_ERR_SIZE;
-  if (d.num_heads_q % d.num_heads_kv != 0) return BSA_ERR_GQA;
-  if (d.num_heads_kv > 65536) return BSA_ERR_TOO_LARGE;  // page offsets are 32-bit
-  const int group = d.num_heads_q / d.num_heads_kv;
-  if (group < 1 || group > 16) return BSA_ERR_GQA;
-  {
-    uint32_t bits;
-    memcpy(&bits, &d.softmax_scale, sizeof(bits));
-    if ((bits & 0x7f800000u) == 0x7f800000u) return BSA_ERR_SOFTMAX_SCALE;  // inf or NaN
-  }
-  if (d.causal != 0 && d.causal != 1) return BSA_ERR_SIZE;
-  const int mt_grid = (d.max_seqlen_q + kTile - 1) / kTile;
-  if (block_mask != nullptr) {
-    if (d.mask_tiles_q <= 0 || d.mask_tiles_kv <= 0) return BSA_ERR_MASK_SHAPE;
-    if ((int64_t)d.mask_tiles_q * kTile < d.max_seqlen_q) return BSA_ERR_MASK_SHAPE;
-    if (d.mask_tiles_kv > BSA_MAX_KV_TILES) return BSA_ERR_TOO_LARGE;
-  }
-  const int64_t grid = (int64_t)d.batch * d.num_heads_q * mt_grid;
-  if (grid > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
+  const bsa_fp8_dims& d = r.d;
+  const int64_t grid = r.tasks;
   if (grid > 0) {
     if (q == nullptr || kcache == nullptr || vcache == nullptr || qscale == nullptr ||
         kscale == nullptr || vscale == nullptr || cu_seqlens_q == nullptr ||
@@ -637,34 +700,58 @@ int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache, const
   p.block_table = block_table;
   p.seqlens_kv = seqlens_kv;
   p.mask = block_mask;
+  p.sidx = r.sidx;
+  p.slen = r.slen;
+  p.schedule = r.schedule;
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   p.B = d.batch;
   p.T = d.total_q;
   p.Hq = d.num_heads_q;
   p.Hkv = d.num_heads_kv;
-  p.group = group;
+  p.group = r.group;
   p.page_size = page_size;
   p.page_shift = page_size == 64 ? 6 : 5;
   p.max_pages = d.max_pages_per_seq;
   p.mt = d.mask_tiles_q;
   p.mkv = d.mask_tiles_kv;
-  p.mt_grid = mt_grid;
+  p.mt_grid = r.mt_grid;
   p.layout = d.kv_layout;
   p.causal = d.causal;
   p.qk_scale = d.softmax_scale * kLog2e;
+  p.pscale_log2 = log2f(r.p_scale);
+  p.q_tok_stride = r.q_layout == BSA_Q_TND ? d.num_heads_q : 1;
+  p.q_head_stride = r.q_layout == BSA_Q_TND ? 1 : d.total_q;
   p.page_bytes = (uint32_t)page_size * (uint32_t)d.num_heads_kv * kHeadDim;
   p.slot_stride = d.kv_layout == BSA_KV_NHD ? d.num_heads_kv : 1;
   p.head_stride = d.kv_layout == BSA_KV_NHD ? 1 : page_size;
 
-  if (quant_type == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR)
-    hipLaunchKernelGGL(bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR>,
-                       dim3((unsigned)grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
-  else
-    hipLaunchKernelGGL(bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD>,
-                       dim3((unsigned)grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
+  const dim3 grid3((unsigned)grid), block3(kThreads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool list = r.form == bsa::kFormList;
+  if (quant_type == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR) {
+    if (list)
+      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR, kFormList>), grid3, block3, 0, s, p);
+    else
+      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR, 0>), grid3, block3, 0, s, p);
+  } else {
+    if (list)
+      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD, kFormList>), grid3, block3, 0, s, p);
+    else
+      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD, 0>), grid3, block3, 0, s, p);
+  }
   if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
   return BSA_OK;
+}
+
+int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache, const float* qscale,
+                    const float* kscale, const float* vscale, const int32_t* cu_seqlens_q,
+                    const int32_t* block_table, const int32_t* seqlens_kv, const uint8_t* block_mask,
+                    int quant_type, int page_size, const bsa_fp8_dims* dims, void* out, float* lse,
+                    void* stream) {
+  return bsa_fp8_prefill_ex(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
+                            seqlens_kv, block_mask, quant_type, page_size, dims, nullptr, out, lse,
+                            stream);
 }
 
 }  // extern "C"

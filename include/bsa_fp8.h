@@ -82,8 +82,19 @@ typedef enum {
     BSA_ERR_SOFTMAX_SCALE = 9, /* softmax_scale not finite                      */
     BSA_ERR_TOO_LARGE = 10,    /* mask_tiles_kv above BSA_MAX_KV_TILES, or a
                                   grid dimension overflow                       */
-    BSA_ERR_LAUNCH = 11        /* the kernel launch failed                      */
+    BSA_ERR_LAUNCH = 11,       /* the kernel launch failed                      */
+    BSA_ERR_Q_LAYOUT = 12,     /* options->q_layout not a bsa_q_layout          */
+    BSA_ERR_P_SCALE = 13,      /* options->p_scale not 0 and not in (0, 448]    */
+    BSA_ERR_SPARSE_FORM = 14,  /* block_mask and sparse_indices both given, or
+                                  only one of sparse_indices / sparse_seq_len   */
+    BSA_ERR_SCHEDULE = 15      /* schedule_len does not match the task count    */
 } bsa_status;
+
+/* Query layouts ("Quant Block Sparse Attention", "Key parameters": layout_q). */
+typedef enum {
+    BSA_Q_TND = 0, /* q E4M3 [T, Hq, 128], qscale float [T, Hq] */
+    BSA_Q_NTD = 1  /* q E4M3 [Hq, T, 128], qscale float [Hq, T] */
+} bsa_q_layout;
 
 /* Largest block-mask width (KV tiles of 128 keys) a masked call accepts:
  * 4096 tiles = 524288 keys.  A call with block_mask == NULL has no limit. */
@@ -144,10 +155,102 @@ int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache,
                     int quant_type, int page_size, const bsa_fp8_dims* dims,
                     void* out, float* lse, void* stream);
 
+/*
+ * Options of the extended entry point.  A zero-initialised struct selects the
+ * behaviour of bsa_fp8_prefill (TND queries, P-scale 256, block_mask form, no
+ * schedule).
+ *
+ * q_layout        bsa_q_layout of q and qscale.  The output stays TND.
+ * p_scale         Probability quantisation scale ("Quant Block Sparse
+ *                 Attention", "Key parameters": p_scale).  Before the P.V
+ *                 product each probability, taken against the running row
+ *                 maximum, is multiplied by p_scale and rounded to E4M3; the
+ *                 final normalisation divides the factor out again.  0 selects
+ *                 256.  Values above 448 are rejected: the row maximum's
+ *                 probability would then exceed the largest E4M3 value.
+ * sparse_indices  Index-list form of the sparsity ("Quant Block Sparse
+ * sparse_seq_len  Attention", "Sparse indices & PA page table"), device
+ *                 pointers, both NULL or both set; block_mask must then be
+ *                 NULL.  sparse_indices int32 [B, Hq, mask_tiles_q,
+ *                 mask_tiles_kv] holds logical KV tile ids (tile n = keys
+ *                 128n .. 128n+127); sparse_seq_len int32 [B, Hq,
+ *                 mask_tiles_q] says how many leading entries of each row are
+ *                 valid (clipped to 0 .. mask_tiles_kv).  Tiles are visited in
+ *                 list order.  Entries that are negative, at or beyond
+ *                 ceil(Lkv_b/128), or wholly above the causal range of the Q
+ *                 tile select no keys and are skipped.  A tile id must not
+ *                 repeat within a row (caller's contract).
+ * schedule        NULL, or the task order written by bsa_fp8_schedule for the
+ * schedule_len    same sparsity, sequence lengths and dims; schedule_len is
+ *                 then the task count B * Hq * ceil(max_seqlen_q / 128).
+ *                 The order changes which tasks run first, never a result:
+ *                 every task is computed the same way whatever its position.
+ */
+typedef struct {
+    int32_t q_layout;
+    float p_scale;
+    const int32_t* sparse_indices;
+    const int32_t* sparse_seq_len;
+    const int32_t* schedule;
+    int32_t schedule_len;
+} bsa_fp8_options;
+
+/*
+ * bsa_fp8_prefill_ex -- bsa_fp8_prefill with the options above ("Quant Block
+ * Sparse Attention", "Key parameters": layout_q, p_scale, sparse_indices,
+ * sparse_seq_len, metadata).  Arguments as for bsa_fp8_prefill; `options` is a
+ * host pointer and may be NULL (= all defaults).  With the index-list form,
+ * dims->mask_tiles_q and dims->mask_tiles_kv give the list shape (Qb, Kb) and
+ * obey the same checks as the block_mask dimensions.  With q_layout NTD, q is
+ * [Hq, T, 128] and qscale [Hq, T].
+ */
+int bsa_fp8_prefill_ex(const void* q, const void* kcache, const void* vcache,
+                       const float* qscale, const float* kscale, const float* vscale,
+                       const int32_t* cu_seqlens_q, const int32_t* block_table,
+                       const int32_t* seqlens_kv, const uint8_t* block_mask,
+                       int quant_type, int page_size, const bsa_fp8_dims* dims,
+                       const bsa_fp8_options* options, void* out, float* lse,
+                       void* stream);
+
+/*
+ * Scheduling pre-pass ("Quant Block Sparse Attention", "Sparse indices & PA
+ * page table": the metadata that splits the (batch, query head, query block)
+ * tasks between cores is produced on the device, on the same stream, and is
+ * never read back by the host).
+ *
+ * A task is one (sequence b, q-head h, Q tile m) with id
+ * (b * Hq + h) * ceil(max_seqlen_q / 128) + m.  Its cost is the number of KV
+ * tiles the prefill visits for it: active tiles (mask bits, or valid list
+ * entries) below ceil(Lkv_b/128) and inside the causal range, 0 for a Q tile
+ * at or beyond Lq_b.  bsa_fp8_schedule writes every task id once into
+ * `schedule`; entry i is the task that workgroup i of the prefill runs, and
+ * the GPU hands workgroup i to XCD i mod 8 (each XCD has its own L2).  When
+ * Hq is a multiple of 8, XCD x owns the q-heads [x*Hq/8, (x+1)*Hq/8) with all
+ * their sequences and Q tiles; its tasks, sorted by decreasing cost (costs
+ * above 1023 count as 1023), equal costs by increasing id, fill entries x,
+ * x+8, x+16, ...  Otherwise all tasks, sorted the same way, fill the entries
+ * in order.  Long tasks then start first and short ones fill the tail.
+ *
+ * bsa_fp8_schedule_workspace_bytes returns the size of the device workspace
+ * the pass needs (0 for no tasks, -1 for invalid dims).  `workspace` must be a
+ * device buffer of at least that many bytes, 16-byte aligned; its contents on
+ * entry do not matter and on return are unspecified.  `schedule` is int32
+ * [B * Hq * ceil(max_seqlen_q/128)].  block_mask, sparse_indices and
+ * sparse_seq_len as for bsa_fp8_prefill_ex (all NULL = dense); `options` may
+ * be NULL; only its sparse_indices / sparse_seq_len are read.  Two kernels are
+ * enqueued on `stream`.  Errors as for bsa_fp8_prefill_ex, plus
+ * BSA_ERR_NULL_POINTER when workspace or schedule is NULL with tasks present.
+ */
+long long bsa_fp8_schedule_workspace_bytes(const bsa_fp8_dims* dims);
+int bsa_fp8_schedule(const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                     const uint8_t* block_mask, const bsa_fp8_dims* dims,
+                     const bsa_fp8_options* options, void* workspace,
+                     int32_t* schedule, void* stream);
+
 /* Static text for a bsa_status value (never NULL). */
 const char* bsa_fp8_status_string(int status);
 
-/* Library ABI version, currently 1. */
+/* Library ABI version, currently 2. */
 int bsa_fp8_abi_version(void);
 
 #ifdef __cplusplus

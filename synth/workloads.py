@@ -305,6 +305,27 @@ def index_form(problem, order="ascending", seed=0, junk=True):
     return idx, seq_len
 
 
+def topk_index_form(problem, k, seed=0):
+    """Index lists of a fixed capacity k that do not come from a mask: for every
+    Q tile, min(k, ceil(Lkv/128)) distinct KV tiles drawn uniformly from the
+    sequence's tiles, in seeded random order (a top-k style selection that
+    ignores causality: tiles above the causal range select nothing).  Returns
+    (sparse_indices int32 [B,Hq,Mt,k], sparse_seq_len int32 [B,Hq,Mt]), Mt as
+    in the block mask."""
+    B, Hq, Mt, _ = problem.block_mask.shape
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, Hq, Mt, k), -1, dtype=np.int32)
+    seq_len = np.zeros((B, Hq, Mt), dtype=np.int32)
+    for b in range(B):
+        n_tiles = int((problem.seqlens_kv[b] + TILE - 1) // TILE)
+        take = min(k, n_tiles)
+        for h in range(Hq):
+            for m in range(Mt):
+                idx[b, h, m, :take] = rng.permutation(n_tiles)[:take]
+                seq_len[b, h, m] = take
+    return idx, seq_len
+
+
 def to_ntd(problem):
     """Q codes and Q descales in the NTD layout: [Hq,T,128] and [Hq,T]."""
     return (np.ascontiguousarray(problem.q.transpose(1, 0, 2)),

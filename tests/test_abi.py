@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import block_sparse_fp8_amd as bsa
-from block_sparse_fp8_amd import Dims
+from block_sparse_fp8_amd import Dims, Options
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bsa_fp8.h")
@@ -35,11 +35,11 @@ def test_exports_every_declared_symbol(lib):
     assert "bsa_fp8_prefill" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.bsa_fp8_abi_version() == 1
+    assert lib.bsa_fp8_abi_version() == 2
 
 
 def test_status_strings(lib):
-    for s in range(0, 12):
+    for s in range(0, 16):
         assert isinstance(bsa.status_string(s), str) and bsa.status_string(s)
     assert bsa.status_string(999) == "unknown status"
 
@@ -134,3 +134,84 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(4, 2, 128, dtype=torch.uint8)
     with pytest.raises(ValueError):
         bsa.bsa_fp8_prefill(x, x, x, x, x, x, x, x, x, None, 0, 64, max_seqlen_q=4)
+
+
+def call_ex(lib, dims, opts=None, quant=0, page_size=64, mask=FAKE, q=FAKE, out=FAKE):
+    return lib.bsa_fp8_prefill_ex(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mask, quant,
+                                  page_size, ctypes.byref(dims),
+                                  None if opts is None else ctypes.byref(opts), out, FAKE, None)
+
+
+def opts(**kw):
+    return Options(**kw)
+
+
+EX_CASES = [
+    ("BSA_ERR_Q_LAYOUT", dict(q_layout=2), {}),
+    ("BSA_ERR_Q_LAYOUT", dict(q_layout=-1), {}),
+    ("BSA_ERR_P_SCALE", dict(p_scale=-1.0), {}),
+    ("BSA_ERR_P_SCALE", dict(p_scale=448.5), {}),
+    ("BSA_ERR_P_SCALE", dict(p_scale=float("nan")), {}),
+    ("BSA_ERR_P_SCALE", dict(p_scale=float("inf")), {}),
+    ("BSA_ERR_SPARSE_FORM", dict(sparse_indices=0x1000, sparse_seq_len=0x1000), {}),   # + mask
+    ("BSA_ERR_SPARSE_FORM", dict(sparse_indices=0x1000), dict(mask=None)),
+    ("BSA_ERR_SPARSE_FORM", dict(sparse_seq_len=0x1000), dict(mask=None)),
+    ("BSA_ERR_SCHEDULE", dict(schedule=0x1000, schedule_len=3), {}),
+    ("BSA_ERR_MASK_SHAPE", dict(sparse_indices=0x1000, sparse_seq_len=0x1000),
+     dict(mask=None, dims=dict(mask_tiles_q=1))),
+    ("BSA_ERR_TOO_LARGE", dict(sparse_indices=0x1000, sparse_seq_len=0x1000),
+     dict(mask=None, dims=dict(mask_tiles_kv=4097))),
+    ("BSA_ERR_HEAD_DIM", {}, dict(dims=dict(head_dim=64))),
+    ("BSA_ERR_PAGE_SIZE", {}, dict(page_size=48)),
+    ("BSA_ERR_QUANT_TYPE", {}, dict(quant=3)),
+]
+
+
+@pytest.mark.parametrize("name,okw,ckw", EX_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(EX_CASES)])
+def test_ex_static_validation(lib, name, okw, ckw):
+    ckw = dict(ckw)
+    d = good_dims(**ckw.pop("dims", {}))
+    assert call_ex(lib, d, opts(**okw), **ckw) == status_values()[name]
+
+
+def test_ex_accepts_valid_options_without_launch(lib):
+    # batch = 0: every static check runs, nothing is launched.
+    st = status_values()
+    d = good_dims(batch=0)
+    for ps in (0.0, 1e-3, 1.0, 256.0, 300.0, 448.0):
+        assert call_ex(lib, d, opts(p_scale=ps)) == st["BSA_OK"], ps
+    assert call_ex(lib, d, opts(q_layout=1)) == st["BSA_OK"]
+    assert call_ex(lib, d, None) == st["BSA_OK"]
+    assert call_ex(lib, d, opts(sparse_indices=0x1000, sparse_seq_len=0x1000), mask=None) == st["BSA_OK"]
+    # the task count is B * Hq * ceil(max_seqlen_q / 128) = 0 here
+    assert call_ex(lib, d, opts(schedule=0x1000, schedule_len=0)) == st["BSA_OK"]
+    assert call_ex(lib, d, opts(schedule=0x1000, schedule_len=1)) == st["BSA_ERR_SCHEDULE"]
+
+
+def test_schedule_workspace_bytes(lib):
+    d = good_dims()                   # 1 * 8 * 2 = 16 tasks
+    n = lib.bsa_fp8_schedule_workspace_bytes(ctypes.byref(d))
+    assert n >= 16 * 4 * 2 + 1024 * 4 and n % 4 == 0
+    d = good_dims(batch=9, num_heads_q=16, num_heads_kv=16, max_seqlen_q=128 * 100)   # 14400 tasks
+    n = lib.bsa_fp8_schedule_workspace_bytes(ctypes.byref(d))
+    assert n >= 14400 * 8 + 15 * 1024 * 4
+    assert lib.bsa_fp8_schedule_workspace_bytes(ctypes.byref(good_dims(batch=0))) == 0
+    assert lib.bsa_fp8_schedule_workspace_bytes(ctypes.byref(good_dims(head_dim=64))) == -1
+    assert lib.bsa_fp8_schedule_workspace_bytes(None) == -1
+
+
+def test_schedule_static_validation(lib):
+    st = status_values()
+    d = good_dims()
+    z = ctypes.c_void_p(0)
+    sched = lambda dims, mask=FAKE, o=None, ws=FAKE, out=FAKE, cu=FAKE: lib.bsa_fp8_schedule(
+        cu, FAKE, mask, ctypes.byref(dims), None if o is None else ctypes.byref(o), ws, out, None)
+    assert sched(d, ws=z) == st["BSA_ERR_NULL_POINTER"]
+    assert sched(d, out=z) == st["BSA_ERR_NULL_POINTER"]
+    assert sched(d, cu=z) == st["BSA_ERR_NULL_POINTER"]
+    assert sched(d, o=opts(sparse_indices=0x1000, sparse_seq_len=0x1000)) == st["BSA_ERR_SPARSE_FORM"]
+    assert sched(good_dims(mask_tiles_q=1)) == st["BSA_ERR_MASK_SHAPE"]
+    assert sched(good_dims(head_dim=64)) == st["BSA_ERR_HEAD_DIM"]
+    # only the sparsity fields of the options are read: a bad layout is ignored
+    assert sched(good_dims(batch=0), o=opts(q_layout=7, p_scale=-1.0)) == st["BSA_OK"]
+    assert sched(good_dims(batch=0), ws=z, out=z, cu=z) == st["BSA_OK"]
