@@ -23,8 +23,9 @@
 //            the block, and each task's rank among the block's tasks of its
 //            bin with smaller id (waves take turns, in order, at a shared LDS
 //            counter per bin).
-//   scan     one workgroup: per-bin totals, an exclusive scan over the bins in
-//            increasing order, then the start of every (block, bin) pair.
+//   scan     one workgroup per share: per-bin totals, an exclusive scan over
+//            the share's bins in increasing order, then the start of every
+//            (block, bin) pair.
 //   scatter  one thread per task: its sorted position start(block, bin) +
 //            rank, mapped to the launch position of its XCD share.
 
@@ -58,6 +59,7 @@ struct SchedParams {
   int N, nblk;
   int nbins;           // kBuckets * shares
   int heads_per_share; // Hq / 8 with shares, else Hq
+  int mask_dwords;     // mask rows start on 4-byte boundaries: read them as dwords
   int Hq, mt_grid, mt, mkv, causal;
 };
 
@@ -81,9 +83,20 @@ __global__ void __launch_bounds__(64 * kCostWaves) sched_cost_kernel(SchedParams
     } else if constexpr (FORM == bsa::kFormMask) {
       n_end = min(n_end, p.mkv);
       const uint8_t* r = p.mask + row * p.mkv;
-      for (int base = 0; base < n_end; base += 64) {
-        const int i = base + lane;
-        cost += __popcll(__ballot(i < n_end && r[i] != 0));
+      if (p.mask_dwords) {
+        // four mask bytes per lane; bytes at or beyond n_end are not counted
+        const uint32_t* rw = reinterpret_cast<const uint32_t*>(r);
+        for (int base = 0; base < n_end; base += 256) {
+          const int i = base + lane * 4;
+          const uint32_t w = i < n_end ? rw[i >> 2] : 0u;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cost += __popcll(__ballot(i + k < n_end && ((w >> (8 * k)) & 0xffu) != 0));
+        }
+      } else {
+        for (int base = 0; base < n_end; base += 64) {
+          const int i = base + lane;
+          cost += __popcll(__ballot(i < n_end && r[i] != 0));
+        }
       }
     } else {
       const int len = min(max(p.slen[row], 0), p.mkv);
@@ -133,44 +146,50 @@ __global__ void __launch_bounds__(kBlockTasks) sched_rank_kernel(SchedParams p) 
   for (int i = tid; i < p.nbins; i += kBlockTasks) p.blockhist[(int64_t)blockIdx.x * p.nbins + i] = cnt[i];
 }
 
-// Thread t owns the nbins/1024 consecutive bins starting at t * nbins/1024.
+// One workgroup per share (a 1024-bin slice of the bins); thread t owns bin
+// share*1024 + t, so every load of a histogram row is coalesced.  A share's
+// tasks start at share * N/8 in sorted order (every share holds N/8 tasks), so
+// the shares are scanned independently.
 __global__ void __launch_bounds__(kBlockTasks) sched_scan_kernel(SchedParams p) {
-  __shared__ int a[kBlockTasks];
-  constexpr int kMaxPer = kMaxBins / kBlockTasks;
+  constexpr int kWaves = kBlockTasks / 64;
+  constexpr int kRows = 8;  // histogram rows loaded together
+  __shared__ int wsum[kWaves];
   const int t = threadIdx.x;
-  const int per = p.nbins / kBlockTasks;
-  const int bin0 = t * per;
-  int tot[kMaxPer];
-  int sum = 0;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int share = (int)blockIdx.x;
+  int32_t* col = p.blockhist + share * kBuckets + t;
+  int tot = 0;
+  for (int blk0 = 0; blk0 < p.nblk; blk0 += kRows) {
+    int v[kRows];
 #pragma unroll
-  for (int k = 0; k < kMaxPer; ++k) {
-    tot[k] = 0;
-    if (k < per)
-      for (int blk = 0; blk < p.nblk; ++blk) tot[k] += p.blockhist[(int64_t)blk * p.nbins + bin0 + k];
-    sum += tot[k];
+    for (int r = 0; r < kRows; ++r) v[r] = blk0 + r < p.nblk ? col[(int64_t)(blk0 + r) * p.nbins] : 0;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) tot += v[r];
   }
-  // inclusive scan of the per-thread sums (Hillis-Steele over 1024 entries)
-  a[t] = sum;
+  // exclusive scan over the share's bins: inside the wave, then wave offsets
+  int x = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  for (int off = 1; off < kBlockTasks; off <<= 1) {
-    const int v = t >= off ? a[t - off] : 0;
-    __syncthreads();
-    a[t] += v;
-    __syncthreads();
-  }
-  int base = a[t] - sum;
+  int before = 0;
 #pragma unroll
-  for (int k = 0; k < kMaxPer; ++k) {
-    if (k < per) {
-      int run = base;
-      for (int blk = 0; blk < p.nblk; ++blk) {
-        int32_t* c = p.blockhist + (int64_t)blk * p.nbins + bin0 + k;
-        const int v = *c;
-        *c = run;
-        run += v;
-      }
+  for (int w = 0; w < kWaves; ++w) before += w < wave ? wsum[w] : 0;
+  int run = share * (p.N / (p.nbins / kBuckets)) + before + x - tot;
+  // start of every (block, bin) pair, written over the counts
+  for (int blk0 = 0; blk0 < p.nblk; blk0 += kRows) {
+    int v[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) v[r] = blk0 + r < p.nblk ? col[(int64_t)(blk0 + r) * p.nbins] : 0;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      if (blk0 + r < p.nblk) col[(int64_t)(blk0 + r) * p.nbins] = run;
+      run += v[r];
     }
-    base += tot[k];
   }
 }
 
@@ -250,6 +269,8 @@ int bsa_fp8_schedule(const int32_t* cu_seqlens_q, const int32_t* seqlens_kv, con
   p.nblk = (int)((r.tasks + kBlockTasks - 1) / kBlockTasks);
   p.nbins = nbins;
   p.heads_per_share = nbins == kMaxBins ? r.d.num_heads_q / kXcds : r.d.num_heads_q;
+  p.mask_dwords = block_mask != nullptr && (r.d.mask_tiles_kv & 3) == 0 &&
+                  (reinterpret_cast<uintptr_t>(block_mask) & 3) == 0;
   p.Hq = r.d.num_heads_q;
   p.mt_grid = r.mt_grid;
   p.mt = r.d.mask_tiles_q;
@@ -265,7 +286,7 @@ int bsa_fp8_schedule(const int32_t* cu_seqlens_q, const int32_t* seqlens_kv, con
   else
     hipLaunchKernelGGL(sched_cost_kernel<bsa::kFormDense>, cost_grid, dim3(64 * kCostWaves), 0, s, p);
   hipLaunchKernelGGL(sched_rank_kernel, dim3((unsigned)p.nblk), dim3(kBlockTasks), 0, s, p);
-  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(kBuckets), 0, s, p);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3((unsigned)(nbins / kBuckets)), dim3(kBlockTasks), 0, s, p);
   hipLaunchKernelGGL(sched_scatter_kernel, dim3((unsigned)((r.tasks + 255) / 256)), dim3(256), 0, s, p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
   return BSA_OK;
