@@ -12,14 +12,18 @@ Sources (cited by page title and section throughout):
   * The hpc-ops block-sparse FP8 attention article (hotelren.com/news/5676318),
     sections "Block-sparse scheduling", "Active tile list",
     "FP8 Tensor Core compute: fixed P-scale quantisation" and "Quick start".
+  * The FlashMLA FP8 sparse decoding article (gitcode.com, FlashMLA deep dive),
+    section "Quant/dequant source" (1x128 tile scales amax/448, optionally
+    rounded up to a power of two).
 
 Contents
   e4m3      -- OCP FP8 E4M3FN codec written from the format definition.
   attention -- exact fp64 oracle, P-emulating oracle, brute-force oracle.
   schedule  -- task costs and the task order of the scheduling pre-pass.
+  quantize  -- FP8 quantisation of Q and the K/V append into the paged cache.
 
 Every function is pinned by `tests/test_oracle_*.py`; the one part with no
 independent pin ("parity unpinned") is agreement with the pages' own
 implementations, whose outputs the pages do not print.
 """
-from . import e4m3, attention, schedule  # noqa: F401
+from . import e4m3, attention, schedule, quantize  # noqa: F401

@@ -5,4 +5,4 @@ caches, page tables, block masks).  It holds none of the attention arithmetic,
 and both the oracle-side tests and the GPU-side tests/benchmark use it.
 """
 from .workloads import (CONFIGS, Problem, make_problem, WorkloadConfig, index_form,  # noqa: F401
-                        topk_index_form, to_ntd)
+                        topk_index_form, to_ntd, append_inputs)

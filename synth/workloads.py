@@ -326,6 +326,39 @@ def topk_index_form(problem, k, seed=0):
     return idx, seq_len
 
 
+def append_inputs(problem, seed=0, spread=True):
+    """bfloat16 inputs of the quantise-and-append step for `problem`'s query
+    chunk: the chunk's Q [T,Hq,128], and K and V [T,Hkv,128] for the same
+    tokens (they land at the tail of each KV sequence), as float32 arrays
+    holding bfloat16 values; plus static descales (kscale [1] for quant type
+    0, vscale [1] or [Hkv]).  N(0,1) values times a per-row magnitude drawn
+    log-uniformly from 2^-20 .. 2^20 (spread=True), with a few all-zero rows;
+    the static descales are fixed numbers, so large rows saturate.  Only random
+    draws and bfloat16 rounding (torch's CPU cast) happen here."""
+    rng = np.random.default_rng(seed)
+    T, Hq, _ = problem.q.shape
+    Hkv = problem.cfg.hkv
+
+    def draw(shape):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if spread:
+            mag = np.exp2(rng.uniform(-20, 20, size=shape[:2])).astype(np.float32)
+            x = x * mag[..., None]
+            zero = rng.random(shape[:2]) < 0.01
+            x[zero] = 0.0
+        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+
+    q = draw((T, Hq, HEAD_DIM))
+    k = draw((T, Hkv, HEAD_DIM))
+    v = draw((T, Hkv, HEAD_DIM))
+    kscale = np.array([0.0125], dtype=np.float32)
+    if problem.quant_type == 1:
+        vscale = rng.uniform(0.01, 0.015, size=Hkv).astype(np.float32)
+    else:
+        vscale = np.array([0.0117], dtype=np.float32)
+    return dict(q=q, k=k, v=v, kscale=kscale, vscale=vscale)
+
+
 def to_ntd(problem):
     """Q codes and Q descales in the NTD layout: [Hq,T,128] and [Hq,T]."""
     return (np.ascontiguousarray(problem.q.transpose(1, 0, 2)),
