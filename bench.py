@@ -155,6 +155,73 @@ def cpu_baseline(p, n_act_total, budget_s):
                       f"host cpu_count={os.cpu_count()}"}
 
 
+def bench_quantize_append(p, args):
+    """Time bsa_fp8_quantize_append over the workload's query chunk: Q to E4M3
+    with per-(token, head) descales, the chunk's K and V appended to the paged
+    cache.  Algorithmic HBM bytes per row of 128 values: 256 read (bf16) and
+    128 written (E4M3), plus a 4-byte descale for Q rows and for K rows of
+    quant type 1."""
+    import torch
+    import block_sparse_fp8_amd as bsa
+    from synth import append_inputs
+
+    a = append_inputs(p, seed=0, spread=False)
+    d = p.to_device("cuda")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    q_in, k_in, v_in = (t(a[n]).to(torch.bfloat16) for n in ("q", "k", "v"))
+    ks, vs = t(a["kscale"]), t(a["vscale"])
+    T, Hq, D = p.q.shape
+    Hkv = p.cfg.hkv
+    q_out = torch.empty((T, Hq, D), dtype=torch.float8_e4m3fn, device="cuda")
+    qs_out = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    kcache_scale = d["kscale"] if p.quant_type == 1 else None
+
+    def step():
+        bsa.bsa_fp8_quantize_append(q_in, k_in, v_in, d["cu_seqlens_q"], d["seqlens_kv"],
+                                    d["block_table"], ks, vs, p.quant_type, p.page_size,
+                                    kcache=d["kcache"], vcache=d["vcache"],
+                                    kscale_cache=kcache_scale, kv_layout=p.kv_layout,
+                                    q_out=q_out, qscale_out=qs_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = np.array([s_.elapsed_time(e_) for s_, e_ in ev])
+    rows_q, rows_kv = T * Hq, T * Hkv
+    nbytes = (rows_q * (256 + 128 + 4) + rows_kv * (256 + 128 + (4 if p.quant_type == 1 else 0))
+              + rows_kv * (256 + 128))
+    med = float(np.median(kernel_ms)) / 1e3
+    res = {
+        "metric": "FP8 quantise-and-append HBM GB/s (algorithmic bytes)",
+        "value": round(nbytes / (wall / args.steps) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, fp8_e4m3 out (fp32 arithmetic)",
+        "data": "synthetic (seeded N(0,1) bfloat16)",
+        "config": {"workload": f"{p.cfg.name} query chunk: {T} tokens, Hq {Hq}, Hkv {Hkv}, "
+                               f"quant {p.quant_type}", "rows": rows_q + 2 * rows_kv,
+                   "bytes_per_launch": nbytes},
+        "kernel_ms_min": round(float(kernel_ms.min()), 4),
+        "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / med / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(nbytes / med / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +233,9 @@ def main():
     ap.add_argument("--form", choices=("mask", "list"), default="mask",
                     help="sparsity argument: the uint8 block mask, or the same tiles as ascending "
                          "index lists (sparse_indices + sparse_seq_len)")
+    ap.add_argument("--op", choices=("prefill", "quantize_append"), default="prefill",
+                    help="prefill (the default, the headline metric), or the FP8 quantise-and-append "
+                         "step that produces its inputs (reported in GB/s against HBM)")
     ap.add_argument("--schedule", action="store_true",
                     help="run the scheduling pre-pass inside every step and launch the prefill "
                          "in its task order")
@@ -198,6 +268,9 @@ def main():
     from synth import make_problem
 
     p = make_problem(args.workload)
+    if args.op == "quantize_append":
+        bench_quantize_append(p, args)
+        return
     n_act, pairs = active_tiles(p)
     d = p.to_device("cuda")
     T, Hq, D = p.q.shape

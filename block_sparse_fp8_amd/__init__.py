@@ -23,6 +23,8 @@ __all__ = [
     "bsa_fp8_prefill_ex",
     "bsa_fp8_schedule",
     "bsa_fp8_schedule_workspace_bytes",
+    "bsa_fp8_quantize_append",
+    "ScaleMode",
     "attention_with_kvcache_blocksparse_prefill_fp8",
     "library_path",
     "load_library",
@@ -51,6 +53,12 @@ class QLayout(enum.IntEnum):
     """Query layouts ("Quant Block Sparse Attention", "Key parameters")."""
     TND = 0  # q [T, Hq, 128], qscale [T, Hq]
     NTD = 1  # q [Hq, T, 128], qscale [Hq, T]
+
+
+class ScaleMode(enum.IntEnum):
+    """Descale rule of the quantisation step (FlashMLA FP8 KV-cache article)."""
+    AMAX = 0       # amax / 448
+    AMAX_POW2 = 1  # amax / 448 rounded up to a power of two
 
 
 class BsaError(RuntimeError):
@@ -115,6 +123,10 @@ def load_library():
     lib.bsa_fp8_schedule.argtypes = [vp, vp, vp, ctypes.POINTER(Dims), ctypes.POINTER(Options),
                                      vp, vp, vp]
     lib.bsa_fp8_schedule.restype = ctypes.c_int
+    lib.bsa_fp8_quantize_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.POINTER(Dims),
+                                            vp, vp, vp, vp, vp, vp]
+    lib.bsa_fp8_quantize_append.restype = ctypes.c_int
     lib.bsa_fp8_status_string.argtypes = [ctypes.c_int]
     lib.bsa_fp8_status_string.restype = ctypes.c_char_p
     lib.bsa_fp8_abi_version.argtypes = []
@@ -320,6 +332,75 @@ def bsa_fp8_schedule(cu_seqlens_q, seqlens_kv, block_mask=None, *, num_heads_q, 
     if status != 0:
         raise BsaError(status, status_string(status))
     return schedule
+
+
+def bsa_fp8_quantize_append(q_in, k_in, v_in, cu_seqlens_q, seqlens_kv, block_table, kscale,
+                            vscale, quant_type, page_size, *, kcache, vcache, kscale_cache=None,
+                            kv_layout=KVLayout.NHD, scale_mode=ScaleMode.AMAX, q_out=None,
+                            qscale_out=None, stream=None):
+    """Call the C entry point of the same name: quantise the bfloat16 query
+    chunk (q_in [T,Hq,128]) to E4M3 with per-(token, head) descales, and append
+    the chunk's keys and values (k_in, v_in [T,Hkv,128]) to the paged caches in
+    place (per-token K descales into kscale_cache for quant type 1).  q_in or
+    k_in/v_in may be None to skip that part.  Returns (q_out, qscale_out)."""
+    ref = q_in if q_in is not None else k_in
+    if ref is None:
+        raise ValueError("nothing to do: q_in and k_in are both None")
+    device = ref.device
+    if device.type != "cuda":
+        raise ValueError("bsa_fp8_quantize_append runs on a GPU; input is on " + str(device))
+    for name, t in (("q_in", q_in), ("k_in", k_in), ("v_in", v_in)):
+        if t is not None:
+            _check(name, t, (torch.bfloat16,), device)
+            if t.dim() != 3 or t.shape[2] != 128:
+                raise ValueError(f"{name} must be [T, heads, 128]")
+    kv_layout = KVLayout(int(kv_layout))
+    T = ref.shape[0]
+    Hq = q_in.shape[1] if q_in is not None else 1
+    Hkv = Hq   # without K/V the kv-head count only needs to be a valid GQA ratio
+    if k_in is not None:
+        if v_in is None or v_in.shape != k_in.shape:
+            raise ValueError("k_in and v_in come together, with equal shapes")
+        for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqlens_kv", seqlens_kv),
+                        ("block_table", block_table)):
+            _check(name, t, (torch.int32,), device)
+        _check("kcache", kcache, _FP8, device)
+        _check("vcache", vcache, _FP8, device)
+        _check("vscale", vscale, (torch.float32,), device)
+        if kscale is not None:
+            _check("kscale", kscale, (torch.float32,), device)
+        if kscale_cache is not None:
+            _check("kscale_cache", kscale_cache, (torch.float32,), device)
+        Hkv = k_in.shape[1]
+        if q_in is not None and Hq % Hkv != 0:
+            raise ValueError("num_heads_q must be a multiple of num_heads_kv")
+    if q_in is None:
+        Hq = Hkv
+    B = seqlens_kv.shape[0] if seqlens_kv is not None else 0
+    if q_in is not None:
+        if q_out is None:
+            q_out = torch.empty(q_in.shape, dtype=torch.float8_e4m3fn, device=device)
+        else:
+            _check("q_out", q_out, _FP8, device)
+        if qscale_out is None:
+            qscale_out = torch.empty(q_in.shape[:2], dtype=torch.float32, device=device)
+        else:
+            _check("qscale_out", qscale_out, (torch.float32,), device)
+    dims = Dims(batch=B, total_q=T, num_heads_q=Hq, num_heads_kv=Hkv, head_dim=128,
+                num_pages=kcache.shape[0] if kcache is not None else 0,
+                max_pages_per_seq=block_table.shape[1] if block_table is not None else 0,
+                max_seqlen_q=0, mask_tiles_q=0, mask_tiles_kv=0, kv_layout=int(kv_layout),
+                causal=1, softmax_scale=1.0)
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    status = load_library().bsa_fp8_quantize_append(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(cu_seqlens_q), _ptr(seqlens_kv),
+        _ptr(block_table), _ptr(kscale), _ptr(vscale), int(quant_type), int(page_size),
+        int(scale_mode), ctypes.byref(dims), _ptr(q_out), _ptr(qscale_out), _ptr(kcache),
+        _ptr(vcache), _ptr(kscale_cache), ctypes.c_void_p(stream))
+    if status != 0:
+        raise BsaError(status, status_string(status))
+    return q_out, qscale_out
 
 
 def attention_with_kvcache_blocksparse_prefill_fp8(

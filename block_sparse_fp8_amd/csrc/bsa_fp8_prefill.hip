@@ -662,6 +662,7 @@ const char* bsa_fp8_status_string(int status) {
     case BSA_ERR_P_SCALE: return "p_scale must be 0 (default 256) or in (0, 448]";
     case BSA_ERR_SPARSE_FORM: return "give block_mask or sparse_indices with sparse_seq_len, not both";
     case BSA_ERR_SCHEDULE: return "schedule_len must equal the task count";
+    case BSA_ERR_SCALE_MODE: return "unknown scale_mode";
     default: return "unknown status";
   }
 }

@@ -87,8 +87,16 @@ typedef enum {
     BSA_ERR_P_SCALE = 13,      /* options->p_scale not 0 and not in (0, 448]    */
     BSA_ERR_SPARSE_FORM = 14,  /* block_mask and sparse_indices both given, or
                                   only one of sparse_indices / sparse_seq_len   */
-    BSA_ERR_SCHEDULE = 15      /* schedule_len does not match the task count    */
+    BSA_ERR_SCHEDULE = 15,     /* schedule_len does not match the task count    */
+    BSA_ERR_SCALE_MODE = 16    /* scale_mode not a bsa_scale_mode               */
 } bsa_status;
+
+/* How bsa_fp8_quantize_append computes a descale from a row's largest
+ * magnitude (FlashMLA FP8 KV-cache article, "Quant/dequant source"). */
+typedef enum {
+    BSA_SCALE_AMAX = 0,      /* d = amax / 448 (float32 division)              */
+    BSA_SCALE_AMAX_POW2 = 1  /* d = amax / 448 rounded up to a power of two    */
+} bsa_scale_mode;
 
 /* Query layouts ("Quant Block Sparse Attention", "Key parameters": layout_q). */
 typedef enum {
@@ -246,6 +254,49 @@ int bsa_fp8_schedule(const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
                      const uint8_t* block_mask, const bsa_fp8_dims* dims,
                      const bsa_fp8_options* options, void* workspace,
                      int32_t* schedule, void* stream);
+
+/*
+ * bsa_fp8_quantize_append -- produce the prefill's FP8 inputs from bfloat16
+ * activations: quantise the query chunk and append its keys and values to the
+ * paged cache.  Method (FlashMLA FP8 KV-cache article, "Quant/dequant
+ * source"): a row of 128 values gets the descale d = amax/448 (amax = its
+ * largest magnitude; scale_mode POW2 rounds d up to a power of two; a row of
+ * zeros gets d = 1), and each value is stored as the E4M3 value of x/d,
+ * rounded to nearest even and saturated at 448.  The divisions are IEEE
+ * float32.  Which rows get a computed descale follows the quantisation
+ * schemes of the prefill (bsa_quant_type):
+ *   Q   always, per (token, head): q_out E4M3 [T, Hq, 128] (TND), qscale_out
+ *       float [T, Hq];
+ *   K   quant type 1: per (token, kv-head), descale written to kscale_cache at
+ *       the row's (page, slot, kv-head) place; quant type 0: the given
+ *       per-tensor descale kscale[0];
+ *   V   the given descale: vscale[0] (type 0) or vscale[kv-head] (type 1).
+ * Appending ("Quant Block Sparse Attention", "Key parameters" and "Sparse
+ * indices & PA page table": paged cache, the query chunk at the tail of the
+ * KV sequence): token i of sequence b's chunk (cu_seqlens_q) is stored at
+ * logical position Lkv_b - Lq_b + i (seqlens_kv holds the lengths after the
+ * append), i.e. page block_table[b, pos / page_size], slot pos % page_size,
+ * in dims->kv_layout.  No other slot or descale is written.
+ *
+ * q_in         bf16 [T, Hq, 128], or NULL to skip the queries (q_out and
+ *              qscale_out may then be NULL).
+ * k_in, v_in   bf16 [T, Hkv, 128], both NULL to skip the append.
+ * dims         batch, total_q (T), num_heads_q, num_heads_kv, head_dim,
+ *              max_pages_per_seq, kv_layout are read; the other fields must be
+ *              valid as for bsa_fp8_prefill (their values are not used).
+ * Every array is a device pointer owned by the caller; one kernel is enqueued
+ * on `stream`.  Preconditions as for bsa_fp8_prefill (Lq_b <= Lkv_b, valid
+ * block-table entries for the appended positions, finite inputs, positive
+ * given descales).  Errors: as for bsa_fp8_prefill, plus BSA_ERR_SCALE_MODE;
+ * BSA_ERR_NULL_POINTER when a pointer the requested parts need is NULL or
+ * only one of k_in / v_in is given.
+ */
+int bsa_fp8_quantize_append(const void* q_in, const void* k_in, const void* v_in,
+                            const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                            const int32_t* block_table, const float* kscale, const float* vscale,
+                            int quant_type, int page_size, int scale_mode, const bsa_fp8_dims* dims,
+                            void* q_out, float* qscale_out, void* kcache, void* vcache,
+                            float* kscale_cache, void* stream);
 
 /* Static text for a bsa_status value (never NULL). */
 const char* bsa_fp8_status_string(int status);

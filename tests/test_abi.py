@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 16):
+    for s in range(0, 17):
         assert isinstance(bsa.status_string(s), str) and bsa.status_string(s)
     assert bsa.status_string(999) == "unknown status"
 
@@ -215,3 +215,34 @@ def test_schedule_static_validation(lib):
     # only the sparsity fields of the options are read: a bad layout is ignored
     assert sched(good_dims(batch=0), o=opts(q_layout=7, p_scale=-1.0)) == st["BSA_OK"]
     assert sched(good_dims(batch=0), ws=z, out=z, cu=z) == st["BSA_OK"]
+
+
+def quant_call(lib, dims, q_in=FAKE, k_in=FAKE, v_in=FAKE, kscale=FAKE, kscale_cache=FAKE,
+               q_out=FAKE, qscale_out=FAKE, quant=0, page_size=64, mode=0):
+    return lib.bsa_fp8_quantize_append(q_in, k_in, v_in, FAKE, FAKE, FAKE, kscale, FAKE, quant,
+                                       page_size, mode, ctypes.byref(dims), q_out, qscale_out,
+                                       FAKE, FAKE, kscale_cache, None)
+
+
+def test_quantize_append_static_validation(lib):
+    st = status_values()
+    d = good_dims()
+    z = None
+    assert quant_call(lib, d, mode=2) == st["BSA_ERR_SCALE_MODE"]
+    assert quant_call(lib, d, mode=-1) == st["BSA_ERR_SCALE_MODE"]
+    assert quant_call(lib, d, v_in=z) == st["BSA_ERR_NULL_POINTER"]          # K without V
+    assert quant_call(lib, d, k_in=z) == st["BSA_ERR_NULL_POINTER"]          # V without K
+    assert quant_call(lib, d, kscale=z, quant=0) == st["BSA_ERR_NULL_POINTER"]
+    assert quant_call(lib, d, kscale_cache=z, quant=1) == st["BSA_ERR_NULL_POINTER"]
+    assert quant_call(lib, d, q_out=z) == st["BSA_ERR_NULL_POINTER"]
+    assert quant_call(lib, d, qscale_out=z) == st["BSA_ERR_NULL_POINTER"]
+    assert quant_call(lib, d, page_size=48) == st["BSA_ERR_PAGE_SIZE"]
+    assert quant_call(lib, d, quant=5) == st["BSA_ERR_QUANT_TYPE"]
+    assert quant_call(lib, good_dims(head_dim=64)) == st["BSA_ERR_HEAD_DIM"]
+    assert quant_call(lib, good_dims(num_heads_q=6, num_heads_kv=4)) == st["BSA_ERR_GQA"]
+    assert quant_call(lib, good_dims(batch=0)) == st["BSA_ERR_SIZE"]         # K/V rows need a sequence
+    # nothing to do: no launch, OK
+    assert quant_call(lib, d, q_in=z, k_in=z, v_in=z, q_out=z, qscale_out=z) == st["BSA_OK"]
+    assert quant_call(lib, good_dims(total_q=0)) == st["BSA_OK"]
+    # the parts that are skipped need no pointers
+    assert quant_call(lib, good_dims(total_q=0), k_in=z, v_in=z, kscale=z, kscale_cache=z) == st["BSA_OK"]
