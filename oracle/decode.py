@@ -1,0 +1,87 @@
+"""fp64 oracle of FP8 sparse decode over a paged 656-byte KV cache.
+
+Test infrastructure only (see the package docstring).  Plain NumPy in float64.
+
+What is computed (the FlashMLA FP8 sparse decoding article: section "FP8
+KVCache format" for the cache row, "Quant/dequant source" for dequantisation,
+and its MQA description of the decode step):
+
+  * the attention is multi-query: every query head attends to the same single
+    KV head; the key has 576 dimensions, the value is the first 512 of them;
+  * a cache row (one token) is 656 bytes: 512 E4M3 codes (the first 512 key
+    dimensions, in four 1x128 tiles), then 4 float32 descales (one per tile),
+    then 64 bfloat16 values (dimensions 512..575, kept unquantised);
+  * dequantised key k^ = (code * descale of its tile) for the first 512
+    dimensions, the bfloat16 values for the last 64; v^ = k^[:512];
+  * for query token (b, s) and head h, the attended set is the list
+    indices[b, s, :] of token positions; an entry outside [0, Lkv_b) is
+    skipped, and an entry listed twice counts twice (a plain reading: each
+    entry is one term of the sum);
+  * score_j = softmax_scale * q[b, s, h, :] . k^_j (576 dimensions);
+    O = sum_j softmax_j(score) v^_j; LSE = ln sum_j exp(score_j);
+  * an empty set gives O = 0 and LSE = -FLT_MAX (the convention of "Quant
+    Block Sparse Attention", "Sparse indices & PA page table", for an empty
+    sparse task).
+
+Readings where the article leaves a step open: a token position j of sequence
+b lives in page block_table[b, j // page_size], slot j % page_size (the paged
+cache of the prefill); the LSE is laid out [B, h_q, s_q].
+"""
+import numpy as np
+import torch
+
+from . import e4m3
+
+D_NOPE = 512
+D_ROPE = 64
+D_K = D_NOPE + D_ROPE
+ROW_BYTES = 656
+TILE = 128
+NEG_FLT_MAX = -3.4028234663852886e38
+
+
+def dequant_rows(rows):
+    """uint8 [..., 656] cache rows -> float64 [..., 576] dequantised keys."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    codes = rows[..., :D_NOPE]
+    scales = np.ascontiguousarray(rows[..., D_NOPE:D_NOPE + 16]).view(np.float32).astype(np.float64)
+    rope_bits = np.ascontiguousarray(rows[..., D_NOPE + 16:]).view(np.uint16)
+    rope = torch.from_numpy(rope_bits.astype(np.int16)).view(torch.bfloat16).double().numpy()
+    nope = e4m3.decode(codes) * np.repeat(scales, TILE, axis=-1)
+    return np.concatenate([nope, rope], axis=-1)
+
+
+def gather_rows(kv_cache, block_table, b, positions):
+    """Cache rows of sequence b at logical token positions (all valid)."""
+    page_size = kv_cache.shape[1]
+    pages = np.asarray(block_table[b])[positions // page_size]
+    return kv_cache[pages, positions % page_size].reshape(len(positions), ROW_BYTES)
+
+
+def sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale):
+    """q: float [B, s_q, h_q, 576] (bfloat16 values); kv_cache: uint8
+    [num_pages, page_size, 656] (or [num_pages, page_size, 1, 656]);
+    indices: int [B, s_q, topk]; block_table: int [B, max_pages];
+    seqlens_kv: int [B].  Returns (O float64 [B, s_q, h_q, 512],
+    LSE float64 [B, h_q, s_q])."""
+    q = np.asarray(q, dtype=np.float64)
+    kv_cache = np.asarray(kv_cache, dtype=np.uint8)
+    kv_cache = kv_cache.reshape(kv_cache.shape[0], kv_cache.shape[1], ROW_BYTES)
+    B, s_q, h_q, _ = q.shape
+    out = np.zeros((B, s_q, h_q, D_NOPE))
+    lse = np.full((B, h_q, s_q), NEG_FLT_MAX)
+    for b in range(B):
+        lkv = int(seqlens_kv[b])
+        for s in range(s_q):
+            idx = np.asarray(indices[b, s], dtype=np.int64)
+            idx = idx[(idx >= 0) & (idx < lkv)]
+            if idx.size == 0:
+                continue
+            k = dequant_rows(gather_rows(kv_cache, block_table, b, idx))      # [n, 576]
+            scores = softmax_scale * (q[b, s] @ k.T)                          # [h, n]
+            mx = scores.max(axis=1, keepdims=True)
+            w = np.exp(scores - mx)
+            l = w.sum(axis=1, keepdims=True)
+            out[b, s] = (w @ k[:, :D_NOPE]) / l
+            lse[b, :, s] = (mx + np.log(l))[:, 0]
+    return out, lse

@@ -6,3 +6,4 @@ and both the oracle-side tests and the GPU-side tests/benchmark use it.
 """
 from .workloads import (CONFIGS, Problem, make_problem, WorkloadConfig, index_form,  # noqa: F401
                         topk_index_form, to_ntd, append_inputs)
+from .decode import DECODE_CONFIGS, DecodeProblem, make_decode_problem  # noqa: F401,E402
