@@ -222,6 +222,68 @@ def bench_quantize_append(p, args):
     print(json.dumps(res), flush=True)
 
 
+PEAK_BF16_TFLOPS = 2500.0                        # MI355X dense bf16 MFMA
+
+
+def bench_decode(args):
+    """Time bsa_fp8_sparse_decode.  Work per query token and head: the selected
+    tokens (valid indices) times 2*(576 + 512) FLOP (Q.K over 576 dims, P.V over
+    512), the count the FlashMLA article uses; bytes: 656 per selected token per
+    query token (the gathered cache rows), plus Q and O."""
+    import torch
+    import block_sparse_fp8_amd as bsa
+    from synth import make_decode_problem, DECODE_CONFIGS
+
+    name = args.workload if args.workload in DECODE_CONFIGS else "decode_b128"
+    p = make_decode_problem(name)
+    d = p.to_device("cuda")
+    B, s_q, h_q, _ = p.q.shape
+    valid = ((p.indices >= 0) & (p.indices < p.seqlens_kv[:, None, None])).sum()
+    flop = float(valid) * h_q * 2 * (576 + 512)
+    nbytes = float(valid) * 656 + B * s_q * h_q * (576 * 2 + 512 * 2)
+    out = torch.empty((B, s_q, h_q, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device="cuda")
+
+    def step():
+        bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"], d["seqlens_kv"],
+                                  softmax_scale=p.softmax_scale, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = np.array([s_.elapsed_time(e_) for s_, e_ in ev])
+    med = float(np.median(kernel_ms)) / 1e3
+    res = {
+        "metric": "FP8 sparse decode TFLOPS (selected tokens, 2*(576+512) FLOP per token and head)",
+        "value": round(flop / (wall / args.steps) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp8_e4m3 cache dequantised to bf16, fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1); power-of-two tile descales)",
+        "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "selected_tokens": int(valid),
+                   "query_tokens": B * s_q},
+        "kernel_ms_min": round(float(kernel_ms.min()), 4),
+        "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
+        "kv_gbps_logical": round(nbytes / med / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(flop / med / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flop / med / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,9 +295,11 @@ def main():
     ap.add_argument("--form", choices=("mask", "list"), default="mask",
                     help="sparsity argument: the uint8 block mask, or the same tiles as ascending "
                          "index lists (sparse_indices + sparse_seq_len)")
-    ap.add_argument("--op", choices=("prefill", "quantize_append"), default="prefill",
-                    help="prefill (the default, the headline metric), or the FP8 quantise-and-append "
-                         "step that produces its inputs (reported in GB/s against HBM)")
+    ap.add_argument("--op", choices=("prefill", "quantize_append", "decode"), default="prefill",
+                    help="prefill (the default, the headline metric); the FP8 quantise-and-append "
+                         "step that produces its inputs (GB/s against HBM); or FP8 sparse decode "
+                         "(MQA over 656-byte cache rows, TFLOP/s against the bf16 matrix peak; "
+                         "workload decode_b128 unless --workload names another decode config)")
     ap.add_argument("--schedule", action="store_true",
                     help="run the scheduling pre-pass inside every step and launch the prefill "
                          "in its task order")
@@ -267,6 +331,9 @@ def main():
     import block_sparse_fp8_amd as bsa
     from synth import make_problem
 
+    if args.op == "decode":
+        bench_decode(args)
+        return
     p = make_problem(args.workload)
     if args.op == "quantize_append":
         bench_quantize_append(p, args)

@@ -24,6 +24,8 @@ __all__ = [
     "bsa_fp8_schedule",
     "bsa_fp8_schedule_workspace_bytes",
     "bsa_fp8_quantize_append",
+    "bsa_fp8_sparse_decode",
+    "DecodeDims",
     "ScaleMode",
     "attention_with_kvcache_blocksparse_prefill_fp8",
     "library_path",
@@ -99,6 +101,19 @@ class Options(ctypes.Structure):
     ]
 
 
+class DecodeDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("s_q", ctypes.c_int32),
+        ("num_heads_q", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
 def load_library():
     """Load libbsa_fp8.so (once).  Raises RuntimeError if it is not built."""
     global _lib_handle
@@ -127,6 +142,8 @@ def load_library():
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(Dims),
                                             vp, vp, vp, vp, vp, vp]
     lib.bsa_fp8_quantize_append.restype = ctypes.c_int
+    lib.bsa_fp8_sparse_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DecodeDims), vp, vp, vp]
+    lib.bsa_fp8_sparse_decode.restype = ctypes.c_int
     lib.bsa_fp8_status_string.argtypes = [ctypes.c_int]
     lib.bsa_fp8_status_string.restype = ctypes.c_char_p
     lib.bsa_fp8_abi_version.argtypes = []
@@ -401,6 +418,51 @@ def bsa_fp8_quantize_append(q_in, k_in, v_in, cu_seqlens_q, seqlens_kv, block_ta
     if status != 0:
         raise BsaError(status, status_string(status))
     return q_out, qscale_out
+
+
+def bsa_fp8_sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, *, softmax_scale=None,
+                          out=None, lse=None, return_lse=True, stream=None):
+    """Call the C entry point of the same name: FP8 sparse decode (MQA over a
+    paged cache of 656-byte token rows).  q bf16 [B, s_q, h_q, 576]; kv_cache
+    uint8 [num_pages, page_size, 656] (or with a kv-head axis of 1); indices
+    int32 [B, s_q, topk]; block_table int32 [B, max_pages]; seqlens_kv int32
+    [B].  Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, h_q, s_q])."""
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("bsa_fp8_sparse_decode runs on a GPU; q is on " + str(device))
+    _check("q", q, (torch.bfloat16,), device)
+    _check("kv_cache", kv_cache, (torch.uint8,), device)
+    for name, t in (("indices", indices), ("block_table", block_table), ("seqlens_kv", seqlens_kv)):
+        _check(name, t, (torch.int32,), device)
+    if q.dim() != 4 or q.shape[3] != 576:
+        raise ValueError("q must be [B, s_q, h_q, 576]")
+    if kv_cache.shape[-1] != 656 or kv_cache.dim() not in (3, 4) or \
+            (kv_cache.dim() == 4 and kv_cache.shape[2] != 1):
+        raise ValueError("kv_cache must be [num_pages, page_size, 656] (or [.., .., 1, 656])")
+    B, s_q, h_q, _ = q.shape
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, s_q):
+        raise ValueError("indices must be [B, s_q, topk]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(576)
+    if out is None:
+        out = torch.empty((B, s_q, h_q, 512), dtype=torch.bfloat16, device=device)
+    else:
+        _check("out", out, (torch.bfloat16,), device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=device)
+    elif lse is not None:
+        _check("lse", lse, (torch.float32,), device)
+    dims = DecodeDims(batch=B, s_q=s_q, num_heads_q=h_q, topk=indices.shape[2],
+                      num_pages=kv_cache.shape[0], page_size=kv_cache.shape[1],
+                      max_pages_per_seq=block_table.shape[1], softmax_scale=float(softmax_scale))
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    status = load_library().bsa_fp8_sparse_decode(
+        _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(block_table), _ptr(seqlens_kv),
+        ctypes.byref(dims), _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
+    if status != 0:
+        raise BsaError(status, status_string(status))
+    return out, lse
 
 
 def attention_with_kvcache_blocksparse_prefill_fp8(

@@ -10,7 +10,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 SOURCES = [os.path.join(_HERE, "csrc", "bsa_fp8_prefill.hip"),
            os.path.join(_HERE, "csrc", "bsa_fp8_schedule.hip"),
-           os.path.join(_HERE, "csrc", "bsa_fp8_quantize.hip")]
+           os.path.join(_HERE, "csrc", "bsa_fp8_quantize.hip"),
+           os.path.join(_HERE, "csrc", "bsa_fp8_decode.hip")]
 OUTPUT = os.path.join(_HERE, "libbsa_fp8.so")
 
 # Packed fp32 VALU forms are switched off for all device code.  Device code

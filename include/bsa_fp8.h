@@ -298,6 +298,60 @@ int bsa_fp8_quantize_append(const void* q_in, const void* k_in, const void* v_in
                             void* q_out, float* qscale_out, void* kcache, void* vcache,
                             float* kscale_cache, void* stream);
 
+/*
+ * FP8 sparse decode (the workload of the FlashMLA FP8 sparse decoding article:
+ * section "FP8 KVCache format" and its description of the MQA decode step).
+ *
+ * Multi-query attention: every query head reads the same single KV head.  A
+ * cache row (one token) is 656 bytes: 512 E4M3 codes (key dims 0..511, four
+ * 1x128 tiles), 4 float32 descales (one per tile), 64 bfloat16 values (key
+ * dims 512..575).  Dequantised key k^ = code * descale (dims 0..511) and the
+ * bfloat16 values (dims 512..575); the value is v^ = k^[0..511].  For query
+ * token (b, s) and head h:
+ *   Omega   = the entries of indices[b, s, :] inside [0, Lkv_b) (an entry
+ *             outside selects nothing; an entry listed twice counts twice)
+ *   score_j = softmax_scale * q[b, s, h, :] . k^_j      (576 dims)
+ *   out[b, s, h, :] = sum_{j in Omega} softmax_j(score) v^_j
+ *   lse[b, h, s]    = ln sum_{j in Omega} exp(score_j)
+ * An empty Omega gives out = 0 and lse = -FLT_MAX ("Quant Block Sparse
+ * Attention", "Sparse indices & PA page table": the empty-task convention).
+ * Token position j of sequence b is the row at page block_table[b, j /
+ * page_size], slot j % page_size.  Dequantised values are rounded to bfloat16
+ * and P to bfloat16 before the bfloat16 matrix products, as the article's
+ * kernel does; with power-of-two descales (its reference quantiser) the
+ * dequantisation is exact.
+ */
+typedef struct {
+    int32_t batch;             /* B                                             */
+    int32_t s_q;               /* query tokens per sequence                     */
+    int32_t num_heads_q;       /* h_q, a multiple of 64                         */
+    int32_t topk;              /* entries per index list, >= 1                  */
+    int32_t num_pages;         /* pages of kv_cache                             */
+    int32_t page_size;         /* 32 or 64                                      */
+    int32_t max_pages_per_seq; /* row length of block_table                     */
+    float softmax_scale;       /* finite                                        */
+} bsa_fp8_decode_dims;
+
+/*
+ * q           bf16 [B, s_q, h_q, 576]
+ * kv_cache    uint8 [num_pages, page_size, 656]
+ * indices     int32 [B, s_q, topk], token positions (any order)
+ * block_table int32 [B, max_pages_per_seq]; entries of pages that hold
+ *             positions < Lkv_b must be valid page ids (the first is read
+ *             whenever Lkv_b > 0)
+ * seqlens_kv  int32 [B], Lkv_b
+ * out         bf16 [B, s_q, h_q, 512]; lse float [B, h_q, s_q] or NULL
+ * Device pointers owned by the caller; one kernel on `stream`; nothing is
+ * allocated.  Errors: BSA_ERR_NULL_POINTER, BSA_ERR_SIZE (negative sizes,
+ * topk < 1), BSA_ERR_GQA (h_q not a multiple of 64), BSA_ERR_PAGE_SIZE,
+ * BSA_ERR_SOFTMAX_SCALE, BSA_ERR_TOO_LARGE (grid or row ids past 2^31),
+ * BSA_ERR_LAUNCH.  Rows the index lists do not select are never read, so they
+ * may hold anything.
+ */
+int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* indices,
+                          const int32_t* block_table, const int32_t* seqlens_kv,
+                          const bsa_fp8_decode_dims* dims, void* out, float* lse, void* stream);
+
 /* Static text for a bsa_status value (never NULL). */
 const char* bsa_fp8_status_string(int status);
 

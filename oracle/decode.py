@@ -58,17 +58,20 @@ def gather_rows(kv_cache, block_table, b, positions):
     return kv_cache[pages, positions % page_size].reshape(len(positions), ROW_BYTES)
 
 
-def sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale):
+def sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, with_abs=False):
     """q: float [B, s_q, h_q, 576] (bfloat16 values); kv_cache: uint8
     [num_pages, page_size, 656] (or [num_pages, page_size, 1, 656]);
     indices: int [B, s_q, topk]; block_table: int [B, max_pages];
     seqlens_kv: int [B].  Returns (O float64 [B, s_q, h_q, 512],
-    LSE float64 [B, h_q, s_q])."""
+    LSE float64 [B, h_q, s_q]); with with_abs, also
+    A = sum_j softmax_j |v^_j| (same shape as O), the scale of the error that
+    rounding each probability by a relative amount causes in O."""
     q = np.asarray(q, dtype=np.float64)
     kv_cache = np.asarray(kv_cache, dtype=np.uint8)
     kv_cache = kv_cache.reshape(kv_cache.shape[0], kv_cache.shape[1], ROW_BYTES)
     B, s_q, h_q, _ = q.shape
     out = np.zeros((B, s_q, h_q, D_NOPE))
+    absw = np.zeros((B, s_q, h_q, D_NOPE))
     lse = np.full((B, h_q, s_q), NEG_FLT_MAX)
     for b in range(B):
         lkv = int(seqlens_kv[b])
@@ -83,5 +86,6 @@ def sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale):
             w = np.exp(scores - mx)
             l = w.sum(axis=1, keepdims=True)
             out[b, s] = (w @ k[:, :D_NOPE]) / l
+            absw[b, s] = (w @ np.abs(k[:, :D_NOPE])) / l
             lse[b, :, s] = (mx + np.log(l))[:, 0]
-    return out, lse
+    return (out, lse, absw) if with_abs else (out, lse)

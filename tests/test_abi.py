@@ -246,3 +246,32 @@ def test_quantize_append_static_validation(lib):
     assert quant_call(lib, good_dims(total_q=0)) == st["BSA_OK"]
     # the parts that are skipped need no pointers
     assert quant_call(lib, good_dims(total_q=0), k_in=z, v_in=z, kscale=z, kscale_cache=z) == st["BSA_OK"]
+
+
+def test_sparse_decode_static_validation(lib):
+    from block_sparse_fp8_amd import DecodeDims
+    st = status_values()
+
+    def dd(**kw):
+        d = dict(batch=2, s_q=2, num_heads_q=128, topk=64, num_pages=10, page_size=64,
+                 max_pages_per_seq=4, softmax_scale=0.0417)
+        d.update(kw)
+        return DecodeDims(**d)
+
+    def call_dec(dims, q=FAKE, out=FAKE, dims_ptr=True):
+        return lib.bsa_fp8_sparse_decode(q, FAKE, FAKE, FAKE, FAKE,
+                                         ctypes.byref(dims) if dims_ptr else None, out, FAKE, None)
+
+    assert call_dec(dd(), dims_ptr=False) == st["BSA_ERR_NULL_POINTER"]
+    assert call_dec(dd(num_heads_q=96)) == st["BSA_ERR_GQA"]
+    assert call_dec(dd(num_heads_q=0)) == st["BSA_ERR_SIZE"]
+    assert call_dec(dd(topk=0)) == st["BSA_ERR_SIZE"]
+    assert call_dec(dd(batch=-1)) == st["BSA_ERR_SIZE"]
+    assert call_dec(dd(page_size=16)) == st["BSA_ERR_PAGE_SIZE"]
+    assert call_dec(dd(softmax_scale=float("nan"))) == st["BSA_ERR_SOFTMAX_SCALE"]
+    assert call_dec(dd(num_pages=2 ** 30, page_size=64)) == st["BSA_ERR_TOO_LARGE"]
+    assert call_dec(dd(), q=None) == st["BSA_ERR_NULL_POINTER"]
+    assert call_dec(dd(), out=None) == st["BSA_ERR_NULL_POINTER"]
+    z = ctypes.c_void_p(0)
+    assert lib.bsa_fp8_sparse_decode(z, z, z, z, z, ctypes.byref(dd(batch=0)), z, z, None) == st["BSA_OK"]
+    assert lib.bsa_fp8_sparse_decode(z, z, z, z, z, ctypes.byref(dd(s_q=0)), z, z, None) == st["BSA_OK"]

@@ -1,0 +1,139 @@
+"""GPU parity of FP8 sparse decode against the fp64 oracle.
+
+The kernel's arithmetic fixes the bound: dequantised K and V are exact in
+bfloat16 (E4M3 codes times power-of-two descales), Q is bfloat16, products
+accumulate in fp32, and two roundings remain, each by at most 2^-8 relative
+(bfloat16 keeps 8 significant bits): every probability to bfloat16 before
+P.V, and the output to bfloat16.  So for every element
+|O_gpu - O| <= 2^-8 (A + |O|) with A = sum_j P_j |v_j| (the
+oracle's weighted magnitude), plus a 5% and 1e-6 margin for the fp32
+accumulation and exp2 steps; no element may exceed it.  LSE involves no
+bfloat16 step: rtol 5e-3 / atol 2.5e-5 as for the prefill.  Rows with no
+valid index must be exactly 0 / -FLT_MAX."""
+import numpy as np
+import pytest
+
+from oracle import decode as D
+from synth import make_decode_problem
+from parity_util import L_RTOL, L_ATOL, MAX_FRAC
+
+pytestmark = pytest.mark.gpu
+
+NEG_FLT_MAX = np.float32(-3.4028234663852886e38)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(p):
+    import torch
+    import block_sparse_fp8_amd as bsa
+    d = p.to_device("cuda")
+    o, l = bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"],
+                                     d["seqlens_kv"], softmax_scale=p.softmax_scale)
+    torch.cuda.synchronize()
+    return o.float().double().cpu().numpy(), l.double().cpu().numpy()
+
+
+def compare(go, gl, eo, el, ea, pairs=None):
+    """ea: the oracle's weighted magnitude A; pairs: (b, s) query tokens to
+    compare (default: all)."""
+    if pairs is not None:
+        go = np.stack([go[b, s] for b, s in pairs])
+        eo = np.stack([eo[b, s] for b, s in pairs])
+        ea = np.stack([ea[b, s] for b, s in pairs])
+        gl = np.stack([gl[b, :, s] for b, s in pairs])
+        el = np.stack([el[b, :, s] for b, s in pairs])
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    err = np.abs(go - eo)
+    bound = 2.0 ** -8 * 1.05 * (ea + np.abs(eo)) + 1e-6
+    bad_l = np.abs(gl - el) > L_ATOL + L_RTOL * np.abs(el)
+    empty = el == NEG_FLT_MAX
+    stats = dict(n=int(go.size), over_bound=int((err > bound).sum()),
+                 worst_ratio=float((err / bound).max()), frac_lse=float(bad_l.mean()),
+                 max_abs=float(err.max()), empty=int(empty.sum()))
+    assert stats["over_bound"] == 0, stats
+    assert stats["frac_lse"] <= MAX_FRAC, stats
+    assert np.all(gl[empty] == NEG_FLT_MAX), stats
+    return stats
+
+
+SMALL = [
+    dict(lkv=(300, 1000), s_q=2, h_q=64, topk=200, ragged=True),
+    dict(lkv=(70,), s_q=1, h_q=128, topk=64, page_size=32),
+    dict(lkv=(1500, 40, 333), s_q=3, h_q=64, topk=77, ragged=True),
+    dict(lkv=(20, 500), s_q=1, h_q=64, topk=5),                # top-k below one block
+    dict(lkv=(2048,), s_q=2, h_q=128, topk=2048, page_size=64),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_small_vs_oracle(i):
+    p = make_decode_problem("decode_tiny", seed=500 + i, **SMALL[i])
+    say(f"[gpu] decode small{i} lkv={p.cfg.lkv} s_q={p.cfg.s_q} h_q={p.cfg.h_q} topk={p.cfg.topk}")
+    go, gl = run_gpu(p)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
+
+
+def test_empty_lists_and_sequences():
+    p = make_decode_problem("decode_tiny", seed=510, lkv=(300, 0, 90), s_q=2, h_q=64, topk=40)
+    p.indices[0, 1, :] = -1                          # nothing selected
+    p.indices[2, 0, :] = 90 + np.arange(40)          # everything past the sequence
+    say("[gpu] decode empty lists / empty sequence")
+    go, gl = run_gpu(p)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    compare(go, gl, eo, el, ea)
+    for b, s in ((0, 1), (1, 0), (1, 1), (2, 0)):
+        assert np.all(go[b, s] == 0.0) and np.all(gl[b, :, s] == NEG_FLT_MAX)
+
+
+def test_repeated_entries_count_twice():
+    p = make_decode_problem("decode_tiny", seed=511, lkv=(400,), s_q=1, h_q=64, topk=50)
+    p.indices[0, 0, 25:] = p.indices[0, 0, :25]       # every token listed twice
+    say("[gpu] decode repeated entries")
+    go, gl = run_gpu(p)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    compare(go, gl, eo, el, ea)
+
+
+def test_unselected_rows_never_read():
+    a = make_decode_problem("decode_tiny", seed=512, fill="random")
+    b = make_decode_problem("decode_tiny", seed=512, fill="nan")
+    say("[gpu] decode NaN in unselected rows")
+    oa, la = run_gpu(a)
+    ob, lb = run_gpu(b)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_deterministic():
+    p = make_decode_problem("decode_tiny", seed=513)
+    say("[gpu] decode determinism")
+    o1, l1 = run_gpu(p)
+    o2, l2 = run_gpu(p)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_sampled():
+    p = make_decode_problem("decode_b128")
+    say("[gpu] decode full size B=128 s_q=2 h_q=128 topk=2048 (16 sampled query tokens)")
+    go, gl = run_gpu(p)
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    rng = np.random.default_rng(3)
+    pairs = sorted({(int(rng.integers(0, 128)), int(rng.integers(0, 2))) for _ in range(16)} | {(0, 0), (127, 1)})
+    sub = p
+    eo = np.zeros_like(go)
+    ea = np.zeros_like(go)
+    el = np.zeros_like(gl)
+    for b, s in pairs:
+        one = D.sparse_decode(sub.q[b:b + 1, s:s + 1], sub.kv_cache, sub.indices[b:b + 1, s:s + 1],
+                              sub.block_table[b:b + 1], sub.seqlens_kv[b:b + 1], sub.softmax_scale,
+                              with_abs=True)
+        eo[b, s] = one[0][0, 0]
+        el[b, :, s] = one[1][0, :, 0]
+        ea[b, s] = one[2][0, 0]
+    say(f"[gpu]   ok {compare(go, gl, eo, el, ea, pairs)}")

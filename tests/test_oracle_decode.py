@@ -152,3 +152,17 @@ def test_dense_selection_matches_torch_attention():
         np.testing.assert_allclose(o[b, 0], ref.numpy(), rtol=1e-10, atol=1e-12)
         ref_lse = torch.logsumexp(p.softmax_scale * (q @ k.T), dim=1)
         np.testing.assert_allclose(lse[b, :, 0], ref_lse.numpy(), rtol=1e-12)
+
+
+def test_abs_weighted_output():
+    """A = sum softmax |v| bounds |O| and equals |O| when all values agree in sign."""
+    p = make_decode_problem("decode_tiny", seed=12)
+    o, lse, a = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    assert np.all(a >= np.abs(o) - 1e-12)
+    ps = p.kv_cache.shape[1]
+    for b in range(2):                 # make every value positive: A equals O
+        for j in range(p.seqlens_kv[b]):
+            row = p.kv_cache[p.block_table[b, j // ps], j % ps]
+            row[:512] &= 0x7F            # clear the sign of every code (descales are positive)
+    o, lse, a = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    np.testing.assert_allclose(a, o, rtol=1e-12, atol=0)
