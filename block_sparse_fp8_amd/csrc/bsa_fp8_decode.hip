@@ -6,29 +6,32 @@
 // bfloat16 values) and 512-dim values (the first 512 key dimensions); each
 // query token attends to its own list of top-k token positions.  The article's
 // kernel dequantises K/V to bfloat16 and runs both products on bfloat16 matrix
-// units; the same split holds here.
+// units; the same split holds here.  Its two thread blocks per query token
+// each dequantise half of the rows and exchange them; here one workgroup
+// serves all heads of a query token (up to 128, 16 per wave), so every row is
+// read and dequantised once.
 //
-// One workgroup (4 waves) per (sequence b, query token s, group of 64 heads);
-// the top-k list is walked 32 tokens at a time:
-//   A. gather + dequantise: thread t takes token t/8 of the block and one
-//      eighth of its row (64 E4M3 codes, their descale, 8 bfloat16 values),
-//      converts code * descale to bfloat16 (round to nearest even) and writes
-//      a row-major bfloat16 K tile [32 tokens][576] to LDS.  The row bytes
-//      come from a per-wave LDS staging area that direct-to-LDS loads filled
-//      during the previous block; the row loads of the next block, the page
-//      lookups of the block after it and the index loads of the one after
-//      that are issued here, so a block's memory traffic is in flight during
-//      the blocks before it is used and holds no registers meanwhile.
-//   B. S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: wave w owns heads
-//      16w..16w+15 with Q in registers.  K rows are read in a permuted order
-//      so that each lane ends up holding 8 consecutive tokens of one head,
-//      which is the layout of the P operand below.  Online softmax in the log2
-//      domain (running max and sum per head); P is rounded to bfloat16 into an
-//      LDS buffer [64 heads][32 tokens], with each head's rescale factor.
-//   C. O^T += V^T . P^T: wave w owns output dims 128w..128w+127 for all 64
-//      heads, so each V value is read from LDS once per workgroup.  V^T comes
-//      straight from the row-major K tile through the transposing read
-//      ds_read_b64_tr_b16.
+// Per workgroup (sequence b, query token s, 16*NW heads):
+//   prologue: the cache row of every list entry (page * page_size + slot, or
+//      -1 for an entry outside [0, Lkv)) goes to an LDS list, and Q of each
+//      wave's 16 heads to registers.
+//   The list is then walked 32 tokens at a time; the rows of block n+2 are
+//   fetched while block n is computed, by direct-to-LDS loads into a ring of
+//   three staging buffers (41 chunks of 16 bytes per row, spread over 16
+//   lanes), so the loop issues no other global loads and every wait is an
+//   exact count of them.
+//   A. dequantise: lane (token t, part p) converts codes 32p..32p+31 of its row
+//      (E4M3 -> fp32, times the tile's descale, -> bfloat16, round to nearest
+//      even) into a row-major bfloat16 K tile [32 tokens][576] in LDS, and
+//      copies 8 of the 64 bfloat16 values.
+//   B. S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, wave w owning heads
+//      16w..16w+15.  K rows are read in a permuted order so that each lane
+//      holds 8 consecutive tokens of one head, the layout of the P operand
+//      below.  Online softmax in the log2 domain; P is rounded to bfloat16 into
+//      an LDS buffer [heads][32 tokens], with each head's rescale factor.
+//   C. O^T += V^T . P^T: wave w owns 512/NW output dims for all heads, so each
+//      V value is read from LDS once per workgroup; V^T comes from the
+//      row-major K tile through the transposing read ds_read_b64_tr_b16.
 // Epilogue: O = O_acc / l per head, bfloat16; LSE = ln sum exp(score).  A
 // query with no valid index gets O = 0 and LSE = -FLT_MAX.
 
@@ -42,13 +45,13 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kHeads = 64;          // heads per workgroup
 constexpr int kBlock = 32;          // tokens per iteration
 constexpr int kDimK = 576;
 constexpr int kDimV = 512;
 constexpr int kRowBytes = 656;
 constexpr int kKStride = kDimK * 2 + 16;   // bytes per LDS K row (padded)
+constexpr int kMaxTopk = 8192;             // longest index list (LDS row list)
+constexpr int kStages = 3;                 // staging ring: block n+2 loads while n computes
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegFltMax = -3.402823466e+38f;
@@ -78,42 +81,62 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
 }
 
+// Maximum / sum over lanes l, l^16, l^32, l^48 (the four lane groups holding
+// one head's tokens), on the VALU: each swap returns this lane's value and its
+// partner's.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
                                                   0, 0);
 }
 
-// Direct-to-LDS loads (16 and 4 bytes per lane; a wave writes 64 consecutive
-// elements at the wave-uniform LDS address lds_addr), issued through asm so
-// that the compiler does not make later LDS reads and barriers wait for them;
-// they are waited for explicitly (s_waitcnt vmcnt) before their data is read.
-// M0 is set here and used by nothing else in this kernel.
+// Direct-to-LDS load, 16 bytes per lane; a wave writes 64 consecutive chunks
+// at the wave-uniform LDS address lds_addr.  Issued through asm so that the
+// compiler does not make later LDS reads and barriers wait for it; every one
+// is waited for explicitly.  M0 is set here and used by nothing else in this
+// kernel.
 __device__ __forceinline__ void dma_lds16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
 }
-__device__ __forceinline__ void dma_lds4(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
-}
-// Workgroup barrier that waits for this wave's LDS operations only; loads from
-// global memory stay in flight across it.
+// Workgroup barrier that waits for this wave's LDS operations only.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Per-wave staging of one thread's share of a token row: slots 0..3 hold its
-// 64 codes (16 bytes per lane each), slot 4 its 8 bfloat16 values, then the
-// descale (4 bytes per lane).
-constexpr int kStageSlot = 64 * 16;
-constexpr int kStageWave = 5 * kStageSlot + 64 * 4;
+// Staging of one block per wave: three rounds of 64 lanes x 16 bytes.  Chunk c
+// of a 656-byte row (41 chunks): c < 32 codes 16c..16c+15 -> lane part c/2,
+// round c%2; c = 32 the four descales -> part 0, round 2; c = 33..40 the
+// bfloat16 values -> part c-32, round 2.
+constexpr int kRound = 64 * 16;
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-bsa_fp8_decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBlock * kKStride];        // 37,376 B
-  __shared__ __attribute__((aligned(16))) uint16_t p_lds[kHeads * kBlock];         // 4 KB
+template <int NW>
+__global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kHeads = 16 * NW;          // heads per workgroup
+  constexpr int kDW = kDimV / NW;          // output dims per wave in P.V
+  constexpr int kDB = kDW / 16;            // 16-dim blocks per wave
+  constexpr int kTokThreads = kThreads / kBlock;  // lanes per token in the gather (16 or 8)
+  static_assert(kTokThreads == 16 || kTokThreads == 8, "gather layout");
+  // load rounds per block and wave (three per 16-lane part)
+  constexpr int kRoundsPerBlock = kTokThreads == 16 ? 3 : 6;
+  constexpr int kWaveStage = kRoundsPerBlock * kRound;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBlock * kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lds[kHeads * kBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[kStages * NW * kWaveStage];
+  __shared__ __attribute__((aligned(16))) int32_t rows_lds[kMaxTopk];
   __shared__ float alpha_lds[kHeads];
   __shared__ float l_lds[kHeads];
-  __shared__ float m_lds[kHeads];
-  __shared__ __attribute__((aligned(16))) uint8_t valid_lds[kBlock];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[4 * kStageWave];   // 21,504 B
+  __shared__ int rescale_lds;   // set when any head of the block needs its O rescaled
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,106 +151,135 @@ bsa_fp8_decode_kernel(DecodeParams p) {
   const int s = bs - b * p.s_q;
   const int h0 = hg * kHeads;
   const int lkv = p.seqlens_kv[b];
-  const int32_t* idx_row = p.indices + (int64_t)bs * p.topk;
   const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+  const int nblocks = lkv > 0 ? (p.topk + kBlock - 1) / kBlock : 0;
 
-  // ---- Q of this wave's 16 heads (B operand of S^T = K.Q^T) -----------------
-  // lane: head 16w + c16, dims 32*ks + 8*G .. +7
-  v4i qreg[18];
+  // ---- prologue: Q to registers, every entry's cache row to LDS --------------
+  v4i qreg[18];  // B operand of S^T = K.Q^T: head 16w + c16, dims 32*ks + 8*G .. +7
   {
     const uint16_t* qp = p.q + ((int64_t)bs * p.h_q + h0 + wave * 16 + c16) * kDimK + 8 * G;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const v4i*>(qp + 32 * ks);
+    // complete here: inside the loop the only loads in flight are the staged
+    // rows, whose waits are counted exactly
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qreg[ks]));
   }
+  if (nblocks > 0) {
+    const int32_t* idx_row = p.indices + (int64_t)bs * p.topk;
+    for (int k = tid; k < nblocks * kBlock; k += kThreads) {  // padded to whole blocks with -1
+      const int idx = k < p.topk ? idx_row[k] : -1;
+      const bool ok = idx >= 0 && idx < lkv;
+      rows_lds[k] = ok ? bt[idx >> p.page_shift] * p.page_size + (idx & (p.page_size - 1)) : -1;
+    }
+  }
+  __syncthreads();
 
-  v4f oacc[8][4];  // [dim block][head block]: dims 128w + 16*db + 4G .. +3, head 16*hb + c16
+  // gather roles: token tok of a block, part (0..15 with 16 lanes per token;
+  // with 8 lanes per token each lane does the work of parts 2*part, 2*part+1)
+  const int tok = tid / kTokThreads;
+  const int part = tid % kTokThreads;
+  const int fallback_row = lkv > 0 ? bt[0] * p.page_size : 0;  // position 0: always readable
+  auto row_of = [&](int n) -> int { return n < nblocks ? rows_lds[n * kBlock + tok] : -1; };
+  const uint32_t stage_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage_lds) + wave * kWaveStage;
+  // Issue the loads of block n into staging buffer n % 3: the same number of
+  // load instructions (kRoundsPerBlock) for every block, so waits can count.
+  auto stage_block = [&](int n) {
+    const int row = row_of(n);
+    const uint8_t* r = p.kv + (int64_t)(row >= 0 ? row : fallback_row) * kRowBytes;
+    const uint32_t dst = stage_base + (uint32_t)(n % kStages) * (NW * kWaveStage);
+    if constexpr (kTokThreads == 16) {
+      dma_lds16(r + 32 * part, dst);
+      dma_lds16(r + 32 * part + 16, dst + kRound);
+      // chunk 32 + part (descales, then the bfloat16 values); parts 9..15 reload chunk 40
+      dma_lds16(r + kDimV + 16 * min(part, 8), dst + 2 * kRound);
+    } else {
+      // 8 lanes per token: lane part takes parts 2*part and 2*part+1 of the 16-lane layout
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+      for (int h = 0; h < 2; ++h) {
+        const int pp = 2 * part + h;
+        dma_lds16(r + 32 * pp, dst + (3 * h) * kRound);
+        dma_lds16(r + 32 * pp + 16, dst + (3 * h + 1) * kRound);
+        dma_lds16(r + kDimV + 16 * min(pp, 8), dst + (3 * h + 2) * kRound);
+      }
+    }
+  };
+
+  v4f oacc[kDB][NW];  // dims kDW*w + 16*db + 4G .. +3, head 16*hb + c16
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) oacc[db][hb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY;  // per head (column c16 of this wave), log2 domain
   float l_run = 0.0f;       // this lane's share of the row sum
 
-  const int nblocks = lkv > 0 ? (p.topk + kBlock - 1) / kBlock : 0;
-
-  // ---- index -> row pipeline for this thread's token (token tid/8 of a block)
-  const int tok = tid >> 3;
-  const int part = tid & 7;
-  // a row that is always readable: position 0 of the sequence
-  const int fallback_row = lkv > 0 ? bt[0] * p.page_size : 0;
-  auto load_index = [&](int n) -> int {
-    const int k = n * kBlock + tok;
-    return (n < nblocks && k < p.topk) ? idx_row[k] : -1;
-  };
-  // row id (page * page_size + slot), or -1 for an entry that selects nothing
-  auto lookup_row = [&](int idx) -> int {
-    const bool ok = idx >= 0 && idx < lkv;
-    const int pg = bt[ok ? (idx >> p.page_shift) : 0];
-    return ok ? pg * p.page_size + (idx & (p.page_size - 1)) : -1;
-  };
-  uint8_t* stage = stage_lds + wave * kStageWave;
-  const uint32_t stage_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage);
-  auto stage_row = [&](int row) {
-    const uint8_t* r = p.kv + (int64_t)(row >= 0 ? row : fallback_row) * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma_lds16(r + part * 64 + 16 * i, stage_addr + i * kStageSlot);
-    dma_lds16(r + kDimV + 16 + 16 * part, stage_addr + 4 * kStageSlot);
-    dma_lds4(r + kDimV + 4 * (part >> 1), stage_addr + 5 * kStageSlot);
-  };
-
-  int row_cur = -1;   // row of block n (being dequantised)
-  int row_next = -1;  // row of block n+1
-  int idx_next2 = -1; // index of block n+2
   if (nblocks > 0) {
-    row_cur = lookup_row(load_index(0));
-    stage_row(row_cur);
-    row_next = lookup_row(load_index(1));
-    idx_next2 = load_index(2);
+    stage_block(0);
+    stage_block(1);
   }
 
   for (int n = 0; n < nblocks; ++n) {
+    // Lane-derived offsets are recomputed every block from an opaque copy of the
+    // lane id rather than held in registers across the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lG = ln >> 4;
+    const int lc16 = ln & 15;
+    const int ltok = (wave * 64 + ln) / kTokThreads;
+    const int lpart = (wave * 64 + ln) % kTokThreads;
     // ---- A: dequantise block n into the K tile ------------------------------
-    wait_all_loads();  // this block's staged rows and the next lookups have arrived
-    lds_barrier();     // the previous block's K tile and P buffer are no longer read
+    // block n's loads are complete once at most block n+1's remain in flight
+    if constexpr (kRoundsPerBlock == 3)
+      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    lds_barrier();  // the previous block's K tile, P buffer and flag are no longer read
+    if (tid == 0) rescale_lds = 0;
     {
-      uint8_t* dst = k_lds + tok * kKStride;
-      const float scale = *reinterpret_cast<const float*>(stage + 5 * kStageSlot + 4 * lane);
+      const uint8_t* sb = stage_lds + (n % kStages) * (NW * kWaveStage) + wave * kWaveStage;
+      uint8_t* dst = k_lds + ltok * kKStride;
+      // lane of part 0 of this token within the wave (16-lane layout: its round 2
+      // holds the four descales)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4i codes = *reinterpret_cast<const v4i*>(stage + i * kStageSlot + 16 * lane);
-        uint32_t w[8];
+      for (int h = 0; h < (kTokThreads == 16 ? 1 : 2); ++h) {
+        const int pp = kTokThreads == 16 ? lpart : 2 * lpart + h;  // part in the 16-lane layout
+        const uint8_t* rb = sb + 3 * h * kRound;                 // this lane's rounds for pp
+        // the four descales: round 2 of the token's first lane (part 0)
+        const int lane0 = ln & ~(kTokThreads - 1);
+        const float scale = *reinterpret_cast<const float*>(sb + 2 * kRound + 16 * lane0 + 4 * (pp >> 2));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t c = (uint32_t)codes[j];
-          const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
-          const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
-          w[2 * j] = pack_bf16(lo[0] * scale, lo[1] * scale);
-          w[2 * j + 1] = pack_bf16(hi[0] * scale, hi[1] * scale);
+        for (int i = 0; i < 2; ++i) {
+          const v4i codes = *reinterpret_cast<const v4i*>(rb + i * kRound + 16 * ln);
+          uint32_t w[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t c = (uint32_t)codes[j];
+            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+            w[2 * j] = pack_bf16(lo[0] * scale, lo[1] * scale);
+            w[2 * j + 1] = pack_bf16(hi[0] * scale, hi[1] * scale);
+          }
+          *reinterpret_cast<v4i*>(dst + 2 * (32 * pp + 16 * i)) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+          *reinterpret_cast<v4i*>(dst + 2 * (32 * pp + 16 * i + 8)) =
+              v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
         }
-        *reinterpret_cast<v4i*>(dst + 2 * (part * 64 + 16 * i)) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-        *reinterpret_cast<v4i*>(dst + 2 * (part * 64 + 16 * i + 8)) =
-            v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+        if (pp >= 1 && pp <= 8)
+          *reinterpret_cast<v4i*>(dst + 2 * (kDimV + 8 * (pp - 1))) =
+              *reinterpret_cast<const v4i*>(rb + 2 * kRound + 16 * ln);
       }
-      *reinterpret_cast<v4i*>(dst + 2 * (kDimV + 8 * part)) =
-          *reinterpret_cast<const v4i*>(stage + 4 * kStageSlot + 16 * lane);
-      if (part == 0) valid_lds[tok] = row_cur >= 0 ? 1 : 0;
     }
-    // next loads: rows of block n+1 (into the staging area, once this wave's
-    // reads of it are complete), page lookups of block n+2, indices of n+3
+    // block n+2 into the buffer block n-1 used (this wave's reads of it are done)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    row_cur = row_next;
-    if (n + 1 < nblocks) stage_row(row_cur);
-    row_next = lookup_row(idx_next2);
-    idx_next2 = load_index(n + 3);
+    stage_block(n + 2);
     lds_barrier();  // K tile ready
 
     // ---- B: S^T = K . Q^T for heads 16w..16w+15 --------------------------------
     // block c, accumulator row m -> token 8*(m/4) + 4c + m%4; lane (G, c16) then
-    // holds tokens 8G .. 8G+7 of head c16 in s[0][0..3], s[1][0..3].
+    // holds tokens 8G .. 8G+7 of head c16 in sacc[0][0..3], sacc[1][0..3].
     v4f sacc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
     {
-      const int tok0 = 8 * (c16 >> 2) + (c16 & 3);
-      const uint8_t* a0 = k_lds + tok0 * kKStride + 2 * 8 * G;
+      const int tok0 = 8 * (lc16 >> 2) + (lc16 & 3);
+      const uint8_t* a0 = k_lds + tok0 * kKStride + 2 * 8 * lG;
       const uint8_t* a1 = a0 + 4 * kKStride;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
@@ -239,18 +291,17 @@ bsa_fp8_decode_kernel(DecodeParams p) {
     }
     // online softmax for head c16 over tokens 8G..8G+7
     {
-      const uint64_t vbits = *reinterpret_cast<const uint64_t*>(valid_lds + 8 * G);
+      // rows of tokens 8G..8G+7 (-1: the entry selects nothing)
+      const v4i rv0 = *reinterpret_cast<const v4i*>(rows_lds + n * kBlock + 8 * lG);
+      const v4i rv1 = *reinterpret_cast<const v4i*>(rows_lds + n * kBlock + 8 * lG + 4);
       float x[8];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = (vbits >> (8 * (4 * c + r))) & 0xff;
-          x[4 * c + r] = ok ? sacc[c][r] * p.score_scale : -INFINITY;
-        }
+      for (int r = 0; r < 4; ++r) {
+        x[r] = rv0[r] >= 0 ? sacc[0][r] * p.score_scale : -INFINITY;
+        x[4 + r] = rv1[r] >= 0 ? sacc[1][r] * p.score_scale : -INFINITY;
+      }
       float bmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      bmax = max_over_groups(bmax);
       const float m_new = fmaxf(m_run, bmax);
       const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);  // 0 while nothing was seen
@@ -265,49 +316,52 @@ bsa_fp8_decode_kernel(DecodeParams p) {
       m_run = m_new;
       const v4i pk = v4i{(int)pack_bf16(e[0], e[1]), (int)pack_bf16(e[2], e[3]), (int)pack_bf16(e[4], e[5]),
                          (int)pack_bf16(e[6], e[7])};
-      *reinterpret_cast<v4i*>(p_lds + (wave * 16 + c16) * kBlock + 8 * G) = pk;
-      if (G == 0) alpha_lds[wave * 16 + c16] = alpha;
+      *reinterpret_cast<v4i*>(p_lds + (wave * 16 + lc16) * kBlock + 8 * lG) = pk;
+      if (lG == 0) alpha_lds[wave * 16 + lc16] = alpha;
+      if (lG == 0 && alpha != 1.0f) rescale_lds = 1;  // some head's maximum moved
     }
     lds_barrier();  // P and rescale factors ready
 
-    // ---- C: O^T += V^T . P^T for dims 128w.., all 64 heads -----------------------
+    // ---- C: O^T += V^T . P^T for this wave's dims, all heads ---------------------
     {
-      float al[4];
+      if (rescale_lds) {  // uniform: skipped once no head's maximum moves any more
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) al[hb] = alpha_lds[16 * hb + c16];
+        for (int hb = 0; hb < NW; ++hb) {
+          const float al = alpha_lds[16 * hb + lc16];
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) oacc[db][hb] *= al[hb];
-      v4i pb[4];
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) pb[hb] = *reinterpret_cast<const v4i*>(p_lds + (16 * hb + c16) * kBlock + 8 * G);
+          for (int db = 0; db < kDB; ++db) oacc[db][hb] *= al;
+        }
+      }
       // transposing reads: source lane (G, j) addresses token 8G + j/4 (+4),
       // dims d0 + 4*(j%4); result lane (G, i) then holds dim d0 + i of tokens
       // 8G .. 8G+7
-      const uint8_t* vbase = k_lds + (8 * G + (c16 >> 2)) * kKStride + 2 * (128 * wave + 4 * (c16 & 3));
+      const uint8_t* vbase = k_lds + (8 * lG + (lc16 >> 2)) * kKStride + 2 * (kDW * wave + 4 * (lc16 & 3));
+      constexpr int kHChunk = NW < 4 ? NW : 4;  // head blocks whose P operands are held at once
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 2 * 16 * db));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 4 * kKStride + 2 * 16 * db));
-        const v2i l2 = __builtin_bit_cast(v2i, lo);
-        const v2i h2 = __builtin_bit_cast(v2i, hi);
-        const v4i va = v4i{l2[0], l2[1], h2[0], h2[1]};
+      for (int h0b = 0; h0b < NW; h0b += kHChunk) {
+        v4i pb[kHChunk];
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma_bf16(va, pb[hb], oacc[db][hb]);
+        for (int j = 0; j < kHChunk; ++j)
+          pb[j] = *reinterpret_cast<const v4i*>(p_lds + (16 * (h0b + j) + lc16) * kBlock + 8 * lG);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 2 * 16 * db));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 4 * kKStride + 2 * 16 * db));
+          const v2i l2 = __builtin_bit_cast(v2i, lo);
+          const v2i h2 = __builtin_bit_cast(v2i, hi);
+          const v4i va = v4i{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+          for (int j = 0; j < kHChunk; ++j) oacc[db][h0b + j] = mfma_bf16(va, pb[j], oacc[db][h0b + j]);
+        }
       }
     }
   }
 
   // ---- epilogue ----------------------------------------------------------------
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  wait_all_loads();  // no load is left in flight when the workgroup ends
+  const float l_tot = sum_over_groups(l_run);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load left in flight when the workgroup ends
   __syncthreads();
-  if (G == 0) {
-    l_lds[wave * 16 + c16] = l_tot;
-    m_lds[wave * 16 + c16] = m_run;
-  }
+  if (G == 0) l_lds[wave * 16 + c16] = l_tot;
   __syncthreads();
   if (p.lse != nullptr && G == 0) {
     const bool empty = !(l_tot > 0.0f);
@@ -315,12 +369,12 @@ bsa_fp8_decode_kernel(DecodeParams p) {
         empty ? kNegFltMax : (m_run + log2f(l_tot)) * kLn2;
   }
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
+  for (int hb = 0; hb < NW; ++hb) {
     const float l = l_lds[16 * hb + c16];
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* op = p.out + ((int64_t)bs * p.h_q + h0 + 16 * hb + c16) * kDimV + 128 * wave + 4 * G;
+    uint16_t* op = p.out + ((int64_t)bs * p.h_q + h0 + 16 * hb + c16) * kDimV + kDW * wave + 4 * G;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < kDB; ++db) {
       const v4f o = oacc[db][hb] * inv;
       *reinterpret_cast<v2i*>(op + 16 * db) = v2i{(int)pack_bf16(o[0], o[1]), (int)pack_bf16(o[2], o[3])};
     }
@@ -339,10 +393,12 @@ int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* in
   if (d.batch < 0 || d.s_q < 0 || d.num_heads_q <= 0 || d.topk <= 0 || d.num_pages < 0 ||
       d.max_pages_per_seq < 0)
     return BSA_ERR_SIZE;
-  if (d.num_heads_q % kHeads != 0) return BSA_ERR_GQA;
+  if (d.num_heads_q % 64 != 0) return BSA_ERR_GQA;
+  if (d.topk > kMaxTopk) return BSA_ERR_TOO_LARGE;
   if (d.page_size != 32 && d.page_size != 64) return BSA_ERR_PAGE_SIZE;
   if (!bsa::finite_float(d.softmax_scale)) return BSA_ERR_SOFTMAX_SCALE;
-  const int64_t grid = (int64_t)d.batch * d.s_q * (d.num_heads_q / kHeads);
+  const int nw = d.num_heads_q % 128 == 0 ? 8 : 4;  // 16 heads per wave
+  const int64_t grid = (int64_t)d.batch * d.s_q * (d.num_heads_q / (16 * nw));
   if (grid > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
   if ((int64_t)d.num_pages * d.page_size > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;  // 32-bit row ids
   if (grid == 0) return BSA_OK;
@@ -366,8 +422,12 @@ int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* in
   p.page_shift = d.page_size == 64 ? 6 : 5;
   p.max_pages = d.max_pages_per_seq;
   p.score_scale = d.softmax_scale * kLog2e;
-  hipLaunchKernelGGL(bsa_fp8_decode_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), p);
+  if (nw == 8)
+    hipLaunchKernelGGL(bsa_fp8_decode_kernel<8>, dim3((unsigned)grid), dim3(512), 0,
+                       static_cast<hipStream_t>(stream), p);
+  else
+    hipLaunchKernelGGL(bsa_fp8_decode_kernel<4>, dim3((unsigned)grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
   return BSA_OK;
 }
