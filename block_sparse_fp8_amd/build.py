@@ -11,7 +11,8 @@ _ROOT = os.path.dirname(_HERE)
 SOURCES = [os.path.join(_HERE, "csrc", "bsa_fp8_prefill.hip"),
            os.path.join(_HERE, "csrc", "bsa_fp8_schedule.hip"),
            os.path.join(_HERE, "csrc", "bsa_fp8_quantize.hip"),
-           os.path.join(_HERE, "csrc", "bsa_fp8_decode.hip")]
+           os.path.join(_HERE, "csrc", "bsa_fp8_decode.hip"),
+           os.path.join(_HERE, "csrc", "bsa_fp8_status.cpp")]
 OUTPUT = os.path.join(_HERE, "libbsa_fp8.so")
 
 # Packed fp32 VALU forms are switched off for all device code.  Device code
