@@ -65,6 +65,7 @@ SMALL = [
     dict(lkv=(1500, 40, 333), s_q=3, h_q=64, topk=77, ragged=True),
     dict(lkv=(20, 500), s_q=1, h_q=64, topk=5),                # top-k below one block
     dict(lkv=(2048,), s_q=2, h_q=128, topk=2048, page_size=64),
+    dict(lkv=(900, 350), s_q=1, h_q=192, topk=300, ragged=True),   # three 64-head groups
 ]
 
 

@@ -243,3 +243,23 @@ def test_full_size_long_schedule():
     p = make_problem("long128k")
     say("[gpu] full long128k schedule")
     np.testing.assert_array_equal(run_schedule(p), oracle_schedule(p))
+
+
+def test_all_options_together():
+    """NTD queries, shuffled index lists with junk, P-scale 64 and a device
+    schedule in one call, against the oracle with the same options."""
+    p = make_problem("tiny", seed=140, **SMALL[3])
+    idx = index_form(p, "shuffled", seed=141, junk=True)
+    say("[gpu] NTD + index lists + p_scale 64 + schedule")
+    sched = run_schedule(p, index_form=idx)
+    go, gl = run_gpu_ex(p, q_layout=1, p_scale=64.0, index_form=idx, schedule=sched)
+    qn, qsn = to_ntd(p)
+    kw = p.oracle_kwargs()
+    kw.update(q=qn, qscale=qsn, block_mask=None, sparse_indices=idx[0], sparse_seq_len=idx[1])
+    eo, el = A.prefill(**kw, mode="emulate", q_layout=A.NTD, p_scale=64.0)
+    xo, _ = A.prefill(**kw, mode="exact", q_layout=A.NTD)
+    say(f"[gpu]   ok {compare(go, gl, eo, el, xo)}")
+    # same bits as the TND call without a schedule
+    to, tl = run_gpu_ex(p, p_scale=64.0, index_form=idx)
+    np.testing.assert_array_equal(go, to)
+    np.testing.assert_array_equal(gl, tl)
