@@ -226,10 +226,11 @@ PEAK_BF16_TFLOPS = 2500.0                        # MI355X dense bf16 MFMA
 
 
 def bench_decode(args):
-    """Time bsa_fp8_sparse_decode.  Work per query token and head: the selected
-    tokens (valid indices) times 2*(576 + 512) FLOP (Q.K over 576 dims, P.V over
-    512), the count the FlashMLA article uses; bytes: 656 per selected token per
-    query token (the gathered cache rows), plus Q and O."""
+    """Time bsa_fp8_sparse_decode (bsa_fp8_sparse_decode_ex when the lists are
+    split into parts).  Work per query token and head: the selected tokens
+    (valid indices) times 2*(576 + 512) FLOP (Q.K over 576 dims, P.V over 512),
+    the count the FlashMLA article uses; bytes: 656 per selected token per query
+    token (the gathered cache rows), plus Q and O."""
     import torch
     import block_sparse_fp8_amd as bsa
     from synth import make_decode_problem, DECODE_CONFIGS
@@ -243,10 +244,20 @@ def bench_decode(args):
     nbytes = float(valid) * 656 + B * s_q * h_q * (576 * 2 + 512 * 2)
     out = torch.empty((B, s_q, h_q, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device="cuda")
+    topk = p.indices.shape[2]
+    splits = (bsa.bsa_fp8_sparse_decode_num_splits(B, s_q, h_q, topk) if args.splits == "auto"
+              else int(args.splits))
+    ws = torch.empty(max(1, bsa.bsa_fp8_sparse_decode_workspace_bytes(B, s_q, h_q, splits)),
+                     dtype=torch.uint8, device="cuda")
 
     def step():
-        bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"], d["seqlens_kv"],
-                                  softmax_scale=p.softmax_scale, out=out, lse=lse)
+        if splits == 1:
+            bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"], d["seqlens_kv"],
+                                      softmax_scale=p.softmax_scale, out=out, lse=lse)
+        else:
+            bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], d["block_table"],
+                                         d["seqlens_kv"], num_splits=splits, workspace=ws,
+                                         softmax_scale=p.softmax_scale, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -273,7 +284,7 @@ def bench_decode(args):
         "dtype": "bf16 (fp8_e4m3 cache dequantised to bf16, fp32 accumulate)",
         "data": "synthetic (seeded N(0,1); power-of-two tile descales)",
         "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "selected_tokens": int(valid),
-                   "query_tokens": B * s_q},
+                   "query_tokens": B * s_q, "num_splits": splits},
         "kernel_ms_min": round(float(kernel_ms.min()), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "kv_gbps_logical": round(nbytes / med / 1e9, 1),
@@ -300,6 +311,9 @@ def main():
                          "step that produces its inputs (GB/s against HBM); or FP8 sparse decode "
                          "(MQA over 656-byte cache rows, TFLOP/s against the bf16 matrix peak; "
                          "workload decode_b128 unless --workload names another decode config)")
+    ap.add_argument("--splits", default="auto",
+                    help="decode only: parts per index list (an integer, or 'auto' for the library's "
+                         "choice; 1 is the single-pass kernel)")
     ap.add_argument("--schedule", action="store_true",
                     help="run the scheduling pre-pass inside every step and launch the prefill "
                          "in its task order")

@@ -25,6 +25,9 @@ __all__ = [
     "bsa_fp8_schedule_workspace_bytes",
     "bsa_fp8_quantize_append",
     "bsa_fp8_sparse_decode",
+    "bsa_fp8_sparse_decode_ex",
+    "bsa_fp8_sparse_decode_workspace_bytes",
+    "bsa_fp8_sparse_decode_num_splits",
     "DecodeDims",
     "ScaleMode",
     "attention_with_kvcache_blocksparse_prefill_fp8",
@@ -144,6 +147,13 @@ def load_library():
     lib.bsa_fp8_quantize_append.restype = ctypes.c_int
     lib.bsa_fp8_sparse_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DecodeDims), vp, vp, vp]
     lib.bsa_fp8_sparse_decode.restype = ctypes.c_int
+    lib.bsa_fp8_sparse_decode_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DecodeDims),
+                                             ctypes.c_int, vp, vp, vp, vp]
+    lib.bsa_fp8_sparse_decode_ex.restype = ctypes.c_int
+    lib.bsa_fp8_sparse_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeDims), ctypes.c_int]
+    lib.bsa_fp8_sparse_decode_workspace_bytes.restype = ctypes.c_longlong
+    lib.bsa_fp8_sparse_decode_num_splits.argtypes = [ctypes.POINTER(DecodeDims)]
+    lib.bsa_fp8_sparse_decode_num_splits.restype = ctypes.c_int
     lib.bsa_fp8_status_string.argtypes = [ctypes.c_int]
     lib.bsa_fp8_status_string.restype = ctypes.c_char_p
     lib.bsa_fp8_abi_version.argtypes = []
@@ -420,13 +430,32 @@ def bsa_fp8_quantize_append(q_in, k_in, v_in, cu_seqlens_q, seqlens_kv, block_ta
     return q_out, qscale_out
 
 
-def bsa_fp8_sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, *, softmax_scale=None,
-                          out=None, lse=None, return_lse=True, stream=None):
-    """Call the C entry point of the same name: FP8 sparse decode (MQA over a
-    paged cache of 656-byte token rows).  q bf16 [B, s_q, h_q, 576]; kv_cache
-    uint8 [num_pages, page_size, 656] (or with a kv-head axis of 1); indices
-    int32 [B, s_q, topk]; block_table int32 [B, max_pages]; seqlens_kv int32
-    [B].  Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, h_q, s_q])."""
+def _decode_dims(batch, s_q, num_heads_q, topk, num_pages=0, page_size=64, max_pages_per_seq=0,
+                 softmax_scale=1.0):
+    return DecodeDims(batch=batch, s_q=s_q, num_heads_q=num_heads_q, topk=topk, num_pages=num_pages,
+                      page_size=page_size, max_pages_per_seq=max_pages_per_seq,
+                      softmax_scale=float(softmax_scale))
+
+
+def bsa_fp8_sparse_decode_workspace_bytes(batch, s_q, num_heads_q, num_splits):
+    """Call the C entry point of the same name: bytes of the split-list
+    decode's workspace (0 for one part)."""
+    dims = _decode_dims(batch, s_q, num_heads_q, 1)
+    n = load_library().bsa_fp8_sparse_decode_workspace_bytes(ctypes.byref(dims), int(num_splits))
+    if n < 0:
+        raise ValueError("invalid sizes or num_splits for the decode workspace")
+    return n
+
+
+def bsa_fp8_sparse_decode_num_splits(batch, s_q, num_heads_q, topk):
+    """Call the C entry point of the same name: a part count that fills the
+    chip and keeps each part's list within one workgroup."""
+    return load_library().bsa_fp8_sparse_decode_num_splits(
+        ctypes.byref(_decode_dims(batch, s_q, num_heads_q, topk)))
+
+
+def _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, out, lse,
+                   return_lse, stream, num_splits, workspace):
     device = q.device
     if device.type != "cuda":
         raise ValueError("bsa_fp8_sparse_decode runs on a GPU; q is on " + str(device))
@@ -452,17 +481,56 @@ def bsa_fp8_sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, *, soft
         lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=device)
     elif lse is not None:
         _check("lse", lse, (torch.float32,), device)
-    dims = DecodeDims(batch=B, s_q=s_q, num_heads_q=h_q, topk=indices.shape[2],
-                      num_pages=kv_cache.shape[0], page_size=kv_cache.shape[1],
-                      max_pages_per_seq=block_table.shape[1], softmax_scale=float(softmax_scale))
+    dims = _decode_dims(B, s_q, h_q, indices.shape[2], kv_cache.shape[0], kv_cache.shape[1],
+                        block_table.shape[1], softmax_scale)
     if stream is None:
         stream = torch.cuda.current_stream(device).cuda_stream
-    status = load_library().bsa_fp8_sparse_decode(
-        _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(block_table), _ptr(seqlens_kv),
-        ctypes.byref(dims), _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
+    lib = load_library()
+    if num_splits is None:
+        status = lib.bsa_fp8_sparse_decode(
+            _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(block_table), _ptr(seqlens_kv),
+            ctypes.byref(dims), _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
+    else:
+        if num_splits == "auto":
+            num_splits = lib.bsa_fp8_sparse_decode_num_splits(ctypes.byref(dims))
+        need = lib.bsa_fp8_sparse_decode_workspace_bytes(ctypes.byref(dims), int(num_splits))
+        if need < 0:
+            raise ValueError(f"num_splits={num_splits} is out of range")
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        elif workspace is not None:
+            _check("workspace", workspace, (torch.uint8,), device)
+            if workspace.numel() < need:
+                raise ValueError(f"workspace holds {workspace.numel()} bytes; {need} are needed")
+        status = lib.bsa_fp8_sparse_decode_ex(
+            _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(block_table), _ptr(seqlens_kv),
+            ctypes.byref(dims), int(num_splits), _ptr(workspace), _ptr(out), _ptr(lse),
+            ctypes.c_void_p(stream))
     if status != 0:
         raise BsaError(status, status_string(status))
     return out, lse
+
+
+def bsa_fp8_sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, *, softmax_scale=None,
+                          out=None, lse=None, return_lse=True, stream=None):
+    """Call the C entry point of the same name: FP8 sparse decode (MQA over a
+    paged cache of 656-byte token rows).  q bf16 [B, s_q, h_q, 576]; kv_cache
+    uint8 [num_pages, page_size, 656] (or with a kv-head axis of 1); indices
+    int32 [B, s_q, topk]; block_table int32 [B, max_pages]; seqlens_kv int32
+    [B].  Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, h_q, s_q])."""
+    return _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, out, lse,
+                          return_lse, stream, None, None)
+
+
+def bsa_fp8_sparse_decode_ex(q, kv_cache, indices, block_table, seqlens_kv, *, num_splits="auto",
+                             workspace=None, softmax_scale=None, out=None, lse=None, return_lse=True,
+                             stream=None):
+    """Call the C entry point of the same name: the sparse decode with each
+    index list cut into num_splits parts ("auto": the library's choice) and
+    merged.  workspace: a uint8 device tensor of at least
+    bsa_fp8_sparse_decode_workspace_bytes bytes, allocated here when None."""
+    return _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, out, lse,
+                          return_lse, stream, num_splits, workspace)
 
 
 def attention_with_kvcache_blocksparse_prefill_fp8(

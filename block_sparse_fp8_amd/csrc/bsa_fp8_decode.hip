@@ -50,7 +50,7 @@ constexpr int kDimK = 576;
 constexpr int kDimV = 512;
 constexpr int kRowBytes = 656;
 constexpr int kKStride = kDimK * 2 + 16;   // bytes per LDS K row (padded)
-constexpr int kMaxTopk = 8192;             // longest index list (LDS row list)
+constexpr int kMaxTopk = BSA_DECODE_MAX_TOPK;  // longest index list one workgroup holds (LDS row list)
 constexpr int kStages = 3;                 // staging ring: block n+2 loads while n computes
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -75,6 +75,10 @@ struct DecodeParams {
   float* lse;                 // [B, h_q, s_q] or nullptr
   int B, s_q, h_q, topk, page_size, page_shift, max_pages;
   float score_scale;          // softmax_scale * log2(e)
+  int num_splits;             // parts of each index list handled by separate workgroups
+  int blocks_per_split;       // 32-token blocks per part
+  float* opart;               // num_splits > 1: [splits, B*s_q, h_q, 512] normalised partial O
+  float* lpart;               // num_splits > 1: [splits, B*s_q, h_q] partial log2-sum-exp (-inf: empty)
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -145,14 +149,19 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   const int c16 = lane & 15;     // column within a 16x16 block
 
   const int groups = p.h_q / kHeads;
-  const int hg = blockIdx.x % groups;
-  const int bs = blockIdx.x / groups;  // b * s_q + s
+  const int split = blockIdx.x % p.num_splits;
+  const int rest = blockIdx.x / p.num_splits;
+  const int hg = rest % groups;
+  const int bs = rest / groups;  // b * s_q + s
   const int b = bs / p.s_q;
   const int s = bs - b * p.s_q;
   const int h0 = hg * kHeads;
   const int lkv = p.seqlens_kv[b];
   const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
-  const int nblocks = lkv > 0 ? (p.topk + kBlock - 1) / kBlock : 0;
+  // this workgroup's part of the list: blocks n_begin .. n_begin + nblocks - 1
+  const int nblocks_all = lkv > 0 ? (p.topk + kBlock - 1) / kBlock : 0;
+  const int n_begin = split * p.blocks_per_split;
+  const int nblocks = max(0, min(nblocks_all - n_begin, p.blocks_per_split));
 
   // ---- prologue: Q to registers, every entry's cache row to LDS --------------
   v4i qreg[18];  // B operand of S^T = K.Q^T: head 16w + c16, dims 32*ks + 8*G .. +7
@@ -166,9 +175,10 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
     for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qreg[ks]));
   }
   if (nblocks > 0) {
-    const int32_t* idx_row = p.indices + (int64_t)bs * p.topk;
+    const int32_t* idx_row = p.indices + (int64_t)bs * p.topk + n_begin * kBlock;
+    const int avail = p.topk - n_begin * kBlock;  // entries of the list from this part on
     for (int k = tid; k < nblocks * kBlock; k += kThreads) {  // padded to whole blocks with -1
-      const int idx = k < p.topk ? idx_row[k] : -1;
+      const int idx = k < avail ? idx_row[k] : -1;
       const bool ok = idx >= 0 && idx < lkv;
       rows_lds[k] = ok ? bt[idx >> p.page_shift] * p.page_size + (idx & (p.page_size - 1)) : -1;
     }
@@ -363,6 +373,24 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   __syncthreads();
   if (G == 0) l_lds[wave * 16 + c16] = l_tot;
   __syncthreads();
+  if (p.num_splits > 1) {
+    // partial result of this part: O normalised by its own sum, and its
+    // log2-sum-exp (-inf when the part selected nothing)
+    const int64_t row0 = ((int64_t)split * p.B * p.s_q + bs) * p.h_q + h0;
+    if (G == 0) {
+      const bool empty = !(l_tot > 0.0f);
+      p.lpart[row0 + wave * 16 + c16] = empty ? -INFINITY : m_run + log2f(l_tot);
+    }
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      const float l = l_lds[16 * hb + c16];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      float* op = p.opart + (row0 + 16 * hb + c16) * kDimV + kDW * wave + 4 * G;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) *reinterpret_cast<v4f*>(op + 16 * db) = oacc[db][hb] * inv;
+    }
+    return;
+  }
   if (p.lse != nullptr && G == 0) {
     const bool empty = !(l_tot > 0.0f);
     p.lse[((int64_t)b * p.h_q + h0 + wave * 16 + c16) * p.s_q + s] =
@@ -381,30 +409,125 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   }
 }
 
+constexpr int kMaxSplits = BSA_DECODE_MAX_SPLITS;
+
+// Merge the parts of each (query token, head): with lse_s the parts' log2-sum-
+// exp and M their maximum, O = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M)
+// and LSE = ln2 * (M + log2 sum_s 2^(lse_s - M)).  One workgroup of 128 threads
+// per row: the weights go through LDS, then each thread sums 4 output dims
+// over the parts.
+__global__ void __launch_bounds__(128) bsa_fp8_decode_combine_kernel(DecodeParams p) {
+  __shared__ float w_lds[kMaxSplits];
+  __shared__ float max_lds[2];
+  const int64_t row = blockIdx.x;  // (b * s_q + s) * h_q + h
+  const int64_t rows = (int64_t)p.B * p.s_q * p.h_q;
+  const int tid = threadIdx.x;
+  const int S = p.num_splits;
+  float mx = -INFINITY;
+  for (int sp = tid; sp < S; sp += 128) {
+    const float l = p.lpart[sp * rows + row];
+    w_lds[sp] = l;
+    mx = fmaxf(mx, l);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) max_lds[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(max_lds[0], max_lds[1]);
+  if (mx != -INFINITY)
+    for (int sp = tid; sp < S; sp += 128) w_lds[sp] = __builtin_amdgcn_exp2f(w_lds[sp] - mx);  // 0: empty part
+  __syncthreads();
+
+  const int d0 = 4 * tid;
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  float wsum = 0.0f;
+  if (mx != -INFINITY) {
+    // eight parts' loads in flight at a time: the pass is bound by reading the partials
+    constexpr int kBatch = 8;
+    for (int sp0 = 0; sp0 < S; sp0 += kBatch) {
+      v4f o[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int sp = min(sp0 + i, S - 1);
+        o[i] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p.opart + (sp * rows + row) * kDimV + d0));
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const float w = sp0 + i < S ? w_lds[sp0 + i] : 0.0f;
+        wsum += w;
+        acc += w * o[i];
+      }
+    }
+  }
+  const int bs = (int)(row / p.h_q);
+  const int h = (int)(row - (int64_t)bs * p.h_q);
+  const int b = bs / p.s_q;
+  const int s = bs - b * p.s_q;
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const v4f o = acc * inv;
+  *reinterpret_cast<v2i*>(p.out + row * kDimV + d0) = v2i{(int)pack_bf16(o[0], o[1]), (int)pack_bf16(o[2], o[3])};
+  if (p.lse != nullptr && tid == 0)
+    p.lse[((int64_t)b * p.h_q + h) * p.s_q + s] = wsum > 0.0f ? (mx + log2f(wsum)) * kLn2 : kNegFltMax;
+}
+
+
+int64_t partial_rows(const bsa_fp8_decode_dims& d) { return (int64_t)d.batch * d.s_q * d.num_heads_q; }
+
 }  // namespace
 
 extern "C" {
 
-int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* indices,
-                          const int32_t* block_table, const int32_t* seqlens_kv,
-                          const bsa_fp8_decode_dims* dims, void* out, float* lse, void* stream) {
+int bsa_fp8_sparse_decode_num_splits(const bsa_fp8_decode_dims* dims) {
+  if (dims == nullptr || dims->num_heads_q <= 0 || dims->num_heads_q % 64 != 0 || dims->topk <= 0) return 1;
+  const int nw = dims->num_heads_q % 128 == 0 ? 8 : 4;
+  const int64_t base = (int64_t)dims->batch * dims->s_q * (dims->num_heads_q / (16 * nw));
+  const int nblocks = (dims->topk + kBlock - 1) / kBlock;
+  // at least enough parts for the row list of each to fit; then enough
+  // workgroups to occupy every CU, with at least 4 blocks per part
+  const int need = (nblocks * kBlock + kMaxTopk - 1) / kMaxTopk;
+  int64_t want = base > 0 ? (256 + base - 1) / base : 1;
+  want = want < (nblocks + 3) / 4 ? want : (nblocks + 3) / 4;
+  int64_t sp = want > need ? want : need;
+  if (sp < 1) sp = 1;
+  if (sp > kMaxSplits) sp = kMaxSplits;
+  return (int)sp;
+}
+
+long long bsa_fp8_sparse_decode_workspace_bytes(const bsa_fp8_decode_dims* dims, int num_splits) {
+  if (dims == nullptr || num_splits < 1 || num_splits > kMaxSplits || dims->batch < 0 || dims->s_q < 0 ||
+      dims->num_heads_q <= 0)
+    return -1;
+  if (num_splits == 1) return 0;
+  return (long long)num_splits * partial_rows(*dims) * (kDimV + 1) * 4;
+}
+
+
+int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t* indices,
+                             const int32_t* block_table, const int32_t* seqlens_kv,
+                             const bsa_fp8_decode_dims* dims, int num_splits, void* workspace, void* out,
+                             float* lse, void* stream) {
   if (dims == nullptr) return BSA_ERR_NULL_POINTER;
   const bsa_fp8_decode_dims d = *dims;
   if (d.batch < 0 || d.s_q < 0 || d.num_heads_q <= 0 || d.topk <= 0 || d.num_pages < 0 ||
       d.max_pages_per_seq < 0)
     return BSA_ERR_SIZE;
   if (d.num_heads_q % 64 != 0) return BSA_ERR_GQA;
-  if (d.topk > kMaxTopk) return BSA_ERR_TOO_LARGE;
+  if (num_splits < 1 || num_splits > kMaxSplits) return BSA_ERR_SIZE;
+  const int nblocks_all = (d.topk + kBlock - 1) / kBlock;
+  const int bps = (nblocks_all + num_splits - 1) / num_splits;
+  if ((int64_t)bps * kBlock > kMaxTopk) return BSA_ERR_TOO_LARGE;  // a part's row list must fit in LDS
   if (d.page_size != 32 && d.page_size != 64) return BSA_ERR_PAGE_SIZE;
   if (!bsa::finite_float(d.softmax_scale)) return BSA_ERR_SOFTMAX_SCALE;
   const int nw = d.num_heads_q % 128 == 0 ? 8 : 4;  // 16 heads per wave
-  const int64_t grid = (int64_t)d.batch * d.s_q * (d.num_heads_q / (16 * nw));
+  const int64_t grid = (int64_t)d.batch * d.s_q * (d.num_heads_q / (16 * nw)) * num_splits;
   if (grid > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
   if ((int64_t)d.num_pages * d.page_size > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;  // 32-bit row ids
   if (grid == 0) return BSA_OK;
   if (q == nullptr || kv_cache == nullptr || indices == nullptr || block_table == nullptr ||
-      seqlens_kv == nullptr || out == nullptr)
+      seqlens_kv == nullptr || out == nullptr || (num_splits > 1 && workspace == nullptr))
     return BSA_ERR_NULL_POINTER;
+  if (num_splits > 1 && partial_rows(d) > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
+  if (num_splits > 1 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return BSA_ERR_SIZE;
 
   DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -422,14 +545,28 @@ int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* in
   p.page_shift = d.page_size == 64 ? 6 : 5;
   p.max_pages = d.max_pages_per_seq;
   p.score_scale = d.softmax_scale * kLog2e;
+  p.num_splits = num_splits;
+  p.blocks_per_split = bps;
+  p.opart = static_cast<float*>(workspace);
+  p.lpart = num_splits > 1 ? p.opart + (int64_t)num_splits * partial_rows(d) * kDimV : nullptr;
   if (nw == 8)
     hipLaunchKernelGGL(bsa_fp8_decode_kernel<8>, dim3((unsigned)grid), dim3(512), 0,
                        static_cast<hipStream_t>(stream), p);
   else
     hipLaunchKernelGGL(bsa_fp8_decode_kernel<4>, dim3((unsigned)grid), dim3(256), 0,
                        static_cast<hipStream_t>(stream), p);
+  if (num_splits > 1)
+    hipLaunchKernelGGL(bsa_fp8_decode_combine_kernel, dim3((unsigned)partial_rows(d)), dim3(128), 0,
+                       static_cast<hipStream_t>(stream), p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
   return BSA_OK;
+}
+
+int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* indices,
+                          const int32_t* block_table, const int32_t* seqlens_kv,
+                          const bsa_fp8_decode_dims* dims, void* out, float* lse, void* stream) {
+  return bsa_fp8_sparse_decode_ex(q, kv_cache, indices, block_table, seqlens_kv, dims, 1, nullptr, out, lse,
+                                  stream);
 }
 
 }  // extern "C"

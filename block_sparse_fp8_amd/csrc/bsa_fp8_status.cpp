@@ -5,7 +5,7 @@
 
 extern "C" {
 
-int bsa_fp8_abi_version(void) { return 2; }
+int bsa_fp8_abi_version(void) { return 3; }
 
 const char* bsa_fp8_status_string(int status) {
   switch (status) {

@@ -344,18 +344,74 @@ typedef struct {
  * Device pointers owned by the caller; one kernel on `stream`; nothing is
  * allocated.  Errors: BSA_ERR_NULL_POINTER, BSA_ERR_SIZE (negative sizes,
  * topk < 1), BSA_ERR_GQA (h_q not a multiple of 64), BSA_ERR_PAGE_SIZE,
- * BSA_ERR_SOFTMAX_SCALE, BSA_ERR_TOO_LARGE (grid or row ids past 2^31),
- * BSA_ERR_LAUNCH.  Rows the index lists do not select are never read, so they
- * may hold anything.
+ * BSA_ERR_SOFTMAX_SCALE, BSA_ERR_TOO_LARGE (topk above BSA_DECODE_MAX_TOPK,
+ * grid or row ids past 2^31), BSA_ERR_LAUNCH.  Rows the index lists do not
+ * select are never read, so they may hold anything.  Equivalent to
+ * bsa_fp8_sparse_decode_ex with num_splits = 1.
  */
+#define BSA_DECODE_MAX_TOPK 8192   /* longest index list one workgroup holds      */
+#define BSA_DECODE_MAX_SPLITS 256
 int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* indices,
                           const int32_t* block_table, const int32_t* seqlens_kv,
                           const bsa_fp8_decode_dims* dims, void* out, float* lse, void* stream);
 
+/*
+ * Split-list sparse decode: the same result as bsa_fp8_sparse_decode, with
+ * each index list cut into num_splits contiguous parts that separate
+ * workgroups attend to, and a second kernel that merges the parts.  This is
+ * the decode kernel's way of occupying the chip when B * s_q is small (the
+ * FlashMLA FP8 sparse decoding article: its launch grid carries a dimension
+ * of "SM parts" beside the heads and s_q, and its decode loop is preceded by
+ * a scheduling-metadata call); it also admits lists longer than
+ * BSA_DECODE_MAX_TOPK (the article quotes runs at topk 16384 and 32768).
+ *
+ * Part p covers list entries [p*E, (p+1)*E) with E = 32 * ceil(ceil(topk/32) /
+ * num_splits); a part may be empty.  For each (b, s, h) part p stores
+ * O_p = its own softmax-weighted value sum and lse_p (log2 domain, -inf when
+ * it selects nothing) in the workspace; the merge with M = max_p lse_p and
+ * w_p = 2^(lse_p - M) writes out = sum_p w_p O_p / sum_p w_p and
+ * lse = ln 2 * (M + log2 sum_p w_p), or out = 0 and lse = -FLT_MAX when every
+ * part is empty.  This is exactly the single-pass softmax regrouped; only the
+ * rounding differs.
+ *
+ * num_splits  1 .. BSA_DECODE_MAX_SPLITS; ceil(ceil(topk/32) / num_splits) * 32
+ *             must not exceed BSA_DECODE_MAX_TOPK
+ * workspace   device memory of bsa_fp8_sparse_decode_workspace_bytes(dims,
+ *             num_splits) bytes, 16-byte aligned, owned by the caller and
+ *             overwritten (NULL allowed when num_splits == 1); calls that share
+ *             a workspace must be ordered on one stream
+ * Other arguments as for bsa_fp8_sparse_decode.  Two kernels on `stream`
+ * (one when num_splits == 1); nothing is allocated.  Errors: as for
+ * bsa_fp8_sparse_decode, plus BSA_ERR_SIZE (num_splits out of range, a
+ * workspace not 16-byte aligned), BSA_ERR_NULL_POINTER (workspace NULL with
+ * num_splits > 1), BSA_ERR_TOO_LARGE (a part longer than BSA_DECODE_MAX_TOPK,
+ * or B * s_q * h_q past 2^31 with num_splits > 1).
+ */
+int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t* indices,
+                             const int32_t* block_table, const int32_t* seqlens_kv,
+                             const bsa_fp8_decode_dims* dims, int num_splits, void* workspace,
+                             void* out, float* lse, void* stream);
+
+/*
+ * Workspace bytes bsa_fp8_sparse_decode_ex needs: 0 for num_splits == 1,
+ * else num_splits * B * s_q * h_q * 513 * 4 (float32 partial outputs and
+ * log-sum-exps).  -1 for NULL dims, negative sizes or num_splits out of range.
+ */
+long long bsa_fp8_sparse_decode_workspace_bytes(const bsa_fp8_decode_dims* dims, int num_splits);
+
+/*
+ * A part count for bsa_fp8_sparse_decode_ex (host only, no device access): the
+ * fewest parts whose row lists fit (at most BSA_DECODE_MAX_TOPK entries each),
+ * raised until the decode grid has about 256 workgroups (one per compute
+ * unit) but never below 4 blocks of 32 entries per part, capped at
+ * BSA_DECODE_MAX_SPLITS.  1 for NULL dims or dims the decode rejects.
+ */
+int bsa_fp8_sparse_decode_num_splits(const bsa_fp8_decode_dims* dims);
+
 /* Static text for a bsa_status value (never NULL). */
 const char* bsa_fp8_status_string(int status);
 
-/* Library ABI version, currently 2. */
+/* Library ABI version, currently 3. */
 int bsa_fp8_abi_version(void);
 
 #ifdef __cplusplus

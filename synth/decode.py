@@ -44,6 +44,9 @@ DECODE_CONFIGS = {
     "decode_b128": DecodeConfig("decode_b128", lkv=(4096,) * 128, s_q=2, h_q=128, topk=2048, seed=2002,
                                 description="B=128, s_q 2, 128 heads, top-k 2048 of 4096 cached tokens, "
                                             "page 64"),
+    "decode_long16k": DecodeConfig("decode_long16k", lkv=(32768,) * 4, s_q=2, h_q=128, topk=16384, seed=2003,
+                                   description="B=4, s_q 2, 128 heads, top-k 16384 of 32768 cached tokens, "
+                                               "page 64 (few query tokens, long lists: the split-list path)"),
 }
 
 

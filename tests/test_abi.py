@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     assert "bsa_fp8_prefill" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.bsa_fp8_abi_version() == 2
+    assert lib.bsa_fp8_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -275,3 +275,65 @@ def test_sparse_decode_static_validation(lib):
     z = ctypes.c_void_p(0)
     assert lib.bsa_fp8_sparse_decode(z, z, z, z, z, ctypes.byref(dd(batch=0)), z, z, None) == st["BSA_OK"]
     assert lib.bsa_fp8_sparse_decode(z, z, z, z, z, ctypes.byref(dd(s_q=0)), z, z, None) == st["BSA_OK"]
+
+
+def test_split_decode_static_validation(lib):
+    from block_sparse_fp8_amd import DecodeDims
+    st = status_values()
+
+    def dd(**kw):
+        d = dict(batch=2, s_q=2, num_heads_q=128, topk=64, num_pages=10, page_size=64,
+                 max_pages_per_seq=4, softmax_scale=0.0417)
+        d.update(kw)
+        return DecodeDims(**d)
+
+    def call_ex(dims, splits, ws=FAKE):
+        return lib.bsa_fp8_sparse_decode_ex(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(dims), splits, ws,
+                                            FAKE, FAKE, None)
+
+    assert call_ex(dd(), 0) == st["BSA_ERR_SIZE"]
+    assert call_ex(dd(), 257) == st["BSA_ERR_SIZE"]
+    assert call_ex(dd(), 2, ws=None) == st["BSA_ERR_NULL_POINTER"]
+    assert call_ex(dd(), 2, ws=ctypes.c_void_p(0x1008)) == st["BSA_ERR_SIZE"]   # not 16-byte aligned
+    # one workgroup holds at most 8192 entries: a list of 16384 needs two parts
+    assert call_ex(dd(topk=16384), 1) == st["BSA_ERR_TOO_LARGE"]
+    assert lib.bsa_fp8_sparse_decode(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(dd(topk=16384)), FAKE, FAKE,
+                                     None) == st["BSA_ERR_TOO_LARGE"]
+    # 8193 entries are 257 blocks: two parts of 129 blocks (4128 entries) fit
+    assert call_ex(dd(topk=8193, batch=0), 2) == st["BSA_OK"]
+    assert call_ex(dd(topk=8193), 1) == st["BSA_ERR_TOO_LARGE"]
+    assert call_ex(dd(topk=2 ** 21 + 1), 256) == st["BSA_ERR_TOO_LARGE"]
+    z = ctypes.c_void_p(0)
+    assert lib.bsa_fp8_sparse_decode_ex(z, z, z, z, z, ctypes.byref(dd(batch=0)), 4, z, z, z, None) == st["BSA_OK"]
+
+
+def test_split_decode_sizes(lib):
+    from block_sparse_fp8_amd import DecodeDims
+
+    def dd(**kw):
+        d = dict(batch=2, s_q=2, num_heads_q=128, topk=2048, num_pages=10, page_size=64,
+                 max_pages_per_seq=4, softmax_scale=0.0417)
+        d.update(kw)
+        return DecodeDims(**d)
+
+    ws = lambda d, n: lib.bsa_fp8_sparse_decode_workspace_bytes(ctypes.byref(d), n)  # noqa: E731
+    assert ws(dd(), 1) == 0
+    assert ws(dd(), 3) == 3 * 2 * 2 * 128 * 513 * 4
+    assert ws(dd(), 0) == -1 and ws(dd(), 257) == -1 and ws(dd(batch=-1), 2) == -1
+    assert lib.bsa_fp8_sparse_decode_workspace_bytes(None, 2) == -1
+    assert bsa.bsa_fp8_sparse_decode_workspace_bytes(1, 2, 64, 5) == 5 * 2 * 64 * 513 * 4
+    ns = lambda **kw: lib.bsa_fp8_sparse_decode_num_splits(ctypes.byref(dd(**kw)))  # noqa: E731
+    # 128 heads are one workgroup per query token; B*s_q = 4 -> 64 parts wanted,
+    # but 2048 entries are 64 blocks, at least 4 per part -> 16
+    assert ns() == 16
+    assert ns(batch=128) == 1                        # 256 workgroups already
+    assert ns(batch=1, s_q=1, topk=65536) == 256     # 2048 blocks: 256 parts of 8
+    assert ns(batch=128, topk=65536) == 8            # the list must fit: 8 parts of 8192
+    assert ns(batch=1, s_q=1, num_heads_q=64, topk=128) == 1
+    assert ns(num_heads_q=96) == 1 and ns(topk=0) == 1
+    assert lib.bsa_fp8_sparse_decode_num_splits(None) == 1
+    for kw in (dict(), dict(batch=1, s_q=1, topk=100000), dict(batch=64, topk=30000)):
+        d = dd(**kw)
+        n = lib.bsa_fp8_sparse_decode_num_splits(ctypes.byref(d))
+        blocks = -(-d.topk // 32)
+        assert 1 <= n <= 256 and -(-blocks // n) * 32 <= 8192

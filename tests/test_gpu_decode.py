@@ -26,12 +26,18 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_gpu(p):
+def run_gpu(p, num_splits=None, workspace=None):
+    """num_splits None: the plain entry point; else the split-list one."""
     import torch
     import block_sparse_fp8_amd as bsa
     d = p.to_device("cuda")
-    o, l = bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"],
-                                     d["seqlens_kv"], softmax_scale=p.softmax_scale)
+    if num_splits is None:
+        o, l = bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"],
+                                         d["seqlens_kv"], softmax_scale=p.softmax_scale)
+    else:
+        o, l = bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], d["block_table"],
+                                            d["seqlens_kv"], num_splits=num_splits, workspace=workspace,
+                                            softmax_scale=p.softmax_scale)
     torch.cuda.synchronize()
     return o.float().double().cpu().numpy(), l.double().cpu().numpy()
 
@@ -118,6 +124,20 @@ def test_deterministic():
     np.testing.assert_array_equal(l1, l2)
 
 
+def sampled_oracle(p, go, gl, pairs):
+    eo = np.zeros_like(go)
+    ea = np.zeros_like(go)
+    el = np.zeros_like(gl)
+    for b, s in pairs:
+        one = D.sparse_decode(p.q[b:b + 1, s:s + 1], p.kv_cache, p.indices[b:b + 1, s:s + 1],
+                              p.block_table[b:b + 1], p.seqlens_kv[b:b + 1], p.softmax_scale,
+                              with_abs=True)
+        eo[b, s] = one[0][0, 0]
+        el[b, :, s] = one[1][0, :, 0]
+        ea[b, s] = one[2][0, 0]
+    return eo, el, ea
+
+
 @pytest.mark.timeout(600)
 def test_full_size_sampled():
     p = make_decode_problem("decode_b128")
@@ -126,15 +146,81 @@ def test_full_size_sampled():
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
     rng = np.random.default_rng(3)
     pairs = sorted({(int(rng.integers(0, 128)), int(rng.integers(0, 2))) for _ in range(16)} | {(0, 0), (127, 1)})
-    sub = p
-    eo = np.zeros_like(go)
-    ea = np.zeros_like(go)
-    el = np.zeros_like(gl)
-    for b, s in pairs:
-        one = D.sparse_decode(sub.q[b:b + 1, s:s + 1], sub.kv_cache, sub.indices[b:b + 1, s:s + 1],
-                              sub.block_table[b:b + 1], sub.seqlens_kv[b:b + 1], sub.softmax_scale,
-                              with_abs=True)
-        eo[b, s] = one[0][0, 0]
-        el[b, :, s] = one[1][0, :, 0]
-        ea[b, s] = one[2][0, 0]
+    eo, el, ea = sampled_oracle(p, go, gl, pairs)
+    say(f"[gpu]   ok {compare(go, gl, eo, el, ea, pairs)}")
+
+
+# ---- split-list path: each list cut into parts, partial results merged ----------
+
+@pytest.mark.parametrize("splits", [2, 3, 7, "auto"])
+@pytest.mark.parametrize("i", [0, 2, 3, 4, 5])
+def test_split_small_vs_oracle(i, splits):
+    """Parts of 1+ blocks, parts that select nothing (top-k 5 is one block, so
+    every part after the first is empty) and ragged lists."""
+    p = make_decode_problem("decode_tiny", seed=500 + i, **SMALL[i])
+    say(f"[gpu] split decode small{i} splits={splits} lkv={p.cfg.lkv} topk={p.cfg.topk}")
+    go, gl = run_gpu(p, num_splits=splits)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
+
+
+def test_split_one_equals_plain_bitwise():
+    p = make_decode_problem("decode_tiny", seed=520, lkv=(700, 1200), s_q=2, h_q=128, topk=500, ragged=True)
+    say("[gpu] split decode num_splits=1 vs plain entry point")
+    a = run_gpu(p)
+    b = run_gpu(p, num_splits=1)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_split_empty_lists_and_sequences():
+    p = make_decode_problem("decode_tiny", seed=521, lkv=(300, 0, 90), s_q=2, h_q=64, topk=100)
+    p.indices[0, 1, :] = -1
+    p.indices[2, 0, :] = 90 + np.arange(100)
+    p.indices[0, 0, 32:] = -1                      # only the first part selects anything
+    say("[gpu] split decode empty lists / empty sequence")
+    go, gl = run_gpu(p, num_splits=4)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    compare(go, gl, eo, el, ea)
+    for b, s in ((0, 1), (1, 0), (1, 1), (2, 0)):
+        assert np.all(go[b, s] == 0.0) and np.all(gl[b, :, s] == NEG_FLT_MAX)
+
+
+def test_split_lists_longer_than_one_workgroup():
+    """10000 entries: above the 8192 one workgroup holds, so at least two parts."""
+    import block_sparse_fp8_amd as bsa
+    p = make_decode_problem("decode_tiny", seed=522, lkv=(12000,), s_q=1, h_q=64, topk=10000, ragged=True)
+    n = bsa.bsa_fp8_sparse_decode_num_splits(1, 1, 64, 10000)
+    assert n >= 2
+    say(f"[gpu] split decode topk=10000 splits={n} and 2")
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    for splits in (n, 2):
+        go, gl = run_gpu(p, num_splits=splits)
+        say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
+
+
+def test_split_reused_workspace():
+    """One workspace for two calls of different sizes; the second call must not
+    see the first one's partial results."""
+    import torch
+    import block_sparse_fp8_amd as bsa
+    a = make_decode_problem("decode_tiny", seed=523, lkv=(2000, 900), s_q=2, h_q=128, topk=1000)
+    b = make_decode_problem("decode_tiny", seed=524, lkv=(50,), s_q=1, h_q=64, topk=40)
+    ws = torch.empty(bsa.bsa_fp8_sparse_decode_workspace_bytes(2, 2, 128, 5), dtype=torch.uint8, device="cuda")
+    say("[gpu] split decode reused workspace")
+    for p in (a, b):
+        go, gl = run_gpu(p, num_splits=5, workspace=ws)
+        eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+        compare(go, gl, eo, el, ea)
+
+
+@pytest.mark.timeout(600)
+def test_split_full_size_long_lists_sampled():
+    import block_sparse_fp8_amd as bsa
+    p = make_decode_problem("decode_long16k")
+    n = bsa.bsa_fp8_sparse_decode_num_splits(4, 2, 128, 16384)
+    say(f"[gpu] split decode full size B=4 s_q=2 h_q=128 topk=16384 splits={n} (all 8 query tokens)")
+    go, gl = run_gpu(p, num_splits=n)
+    pairs = [(b, s) for b in range(4) for s in range(2)]
+    eo, el, ea = sampled_oracle(p, go, gl, pairs)
     say(f"[gpu]   ok {compare(go, gl, eo, el, ea, pairs)}")
