@@ -122,7 +122,9 @@ def active_tiles(p):
 
 
 def cpu_baseline(p, n_act_total, budget_s):
-    """Time the oracle (P-emulating mode, as it stands) on a bounded sample of Q tiles."""
+    """Time the oracle, as it stands, on a bounded sample of Q tiles: two thirds
+    of the budget in its P-emulating mode (the reported value), one third in its
+    exact mode (reported beside it)."""
     from oracle import attention as A
     from synth.workloads import sample_q_tiles
     try:
@@ -134,25 +136,34 @@ def cpu_baseline(p, n_act_total, budget_s):
     rng = np.random.default_rng(3)
     rng.shuffle(tiles)
     kw = p.oracle_kwargs()
-    done, flop = [], 0
-    t_start = time.perf_counter()
-    for tile in tiles:
-        A.prefill(**kw, mode="emulate", tiles=[tile])
-        done.append(tile)
-        if time.perf_counter() - t_start > budget_s:
-            break
-    elapsed = time.perf_counter() - t_start
-    for (b, h, m) in done:
-        lq = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
-        lkv = int(p.seqlens_kv[b])
-        pos_max = lkv - lq + min(m * TILE + TILE - 1, lq - 1)
-        n_end = min((lkv + TILE - 1) // TILE, pos_max // TILE + 1)
-        flop += FLOP_PER_TILE * int((p.block_mask[b, h, m, :n_end] != 0).sum())
-    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+
+    def run(mode, todo, budget):
+        done, flop = [], 0
+        t_start = time.perf_counter()
+        for tile in todo:
+            A.prefill(**kw, mode=mode, tiles=[tile])
+            done.append(tile)
+            if time.perf_counter() - t_start > budget:
+                break
+        elapsed = time.perf_counter() - t_start
+        for (b, h, m) in done:
+            lq = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+            lkv = int(p.seqlens_kv[b])
+            pos_max = lkv - lq + min(m * TILE + TILE - 1, lq - 1)
+            n_end = min((lkv + TILE - 1) // TILE, pos_max // TILE + 1)
+            flop += FLOP_PER_TILE * int((p.block_mask[b, h, m, :n_end] != 0).sum())
+        return flop / elapsed / 1e12, len(done), elapsed
+
+    emu, n_emu, t_emu = run("emulate", tiles, budget_s * 2 / 3)
+    exa, n_exa, t_exa = run("exact", tiles[::-1], budget_s / 3)
+    return {"value": emu, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{len(done)} of {p.num_q_tiles} Q tiles (seeded random order), "
-                      f"P-emulating fp64 NumPy oracle, {elapsed:.1f} s wall; "
-                      f"host cpu_count={os.cpu_count()}"}
+            "sample": f"{n_emu} of {p.num_q_tiles} Q tiles (seeded random order), "
+                      f"P-emulating fp64 NumPy oracle, {t_emu:.1f} s wall; "
+                      f"host cpu_count={os.cpu_count()}",
+            "exact_value": exa,
+            "exact_sample": f"{n_exa} Q tiles from the other end of the same order, exact fp64 mode, "
+                            f"{t_exa:.1f} s wall"}
 
 
 def bench_quantize_append(p, args):
@@ -219,7 +230,36 @@ def bench_quantize_append(p, args):
                      "unit": "GB/s", "frac": round(nbytes / med / 1e9 / PEAK_HBM_GBPS, 4),
                      "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_quantize(p, a, args.cpu_budget)
     print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_quantize(p, a, budget_s):
+    """Time the quantise-and-append oracle, as it stands, on growing prefixes of
+    the first sequence's chunk (the tokens keep their places at the tail of the
+    sequence) until the budget is spent; GB/s over the same algorithmic bytes."""
+    from oracle import quantize as Qz
+    Hq, Hkv = p.q.shape[1], p.cfg.hkv
+    lq0 = int(p.cu_seqlens_q[1] - p.cu_seqlens_q[0])
+    n, best, t_total = 64, None, 0.0
+    while n <= lq0:
+        cu = np.array([0, n], dtype=np.int32)
+        lkv = np.array([int(p.seqlens_kv[0]) - lq0 + n], dtype=np.int32)
+        t0 = time.perf_counter()
+        Qz.quantize_append(a["q"][:n], a["k"][:n], a["v"][:n], cu, lkv, p.block_table[:1], a["kscale"],
+                           a["vscale"], p.quant_type, p.page_size, p.kv_layout, p.kcache, p.vcache,
+                           p.kscale if p.quant_type == 1 else None)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        nbytes = n * (Hq * (256 + 128 + 4) + Hkv * (256 + 128 + (4 if p.quant_type == 1 else 0)) + Hkv * 384)
+        best = (nbytes / dt / 1e9, n, dt)
+        if t_total > budget_s or n == lq0:
+            break
+        n = min(2 * n, lq0)
+    return {"value": best[0], "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{best[1]} of {p.q.shape[0]} tokens of the chunk in one call, {best[2]:.1f} s "
+                      f"(NumPy, single-threaded elementwise work); host cpu_count={os.cpu_count()}"}
 
 
 PEAK_BF16_TFLOPS = 2500.0                        # MI355X dense bf16 MFMA
@@ -292,7 +332,37 @@ def bench_decode(args):
                      "unit": "TFLOP/s", "frac": round(flop / med / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(p, args.cpu_budget)
     print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_decode(p, budget_s):
+    """Time the decode oracle, as it stands, one query token at a time over a
+    seeded sample of the workload's query tokens until the budget is spent."""
+    from oracle import decode as D
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    B, s_q, h_q, _ = p.q.shape
+    order = np.random.default_rng(4).permutation(B * s_q)
+    flop, done = 0.0, 0
+    t0 = time.perf_counter()
+    for i in order:
+        b, s = divmod(int(i), s_q)
+        D.sparse_decode(p.q[b:b + 1, s:s + 1], p.kv_cache, p.indices[b:b + 1, s:s + 1],
+                        p.block_table[b:b + 1], p.seqlens_kv[b:b + 1], p.softmax_scale)
+        idx = p.indices[b, s]
+        flop += float(((idx >= 0) & (idx < p.seqlens_kv[b])).sum()) * h_q * 2 * (576 + 512)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    elapsed = time.perf_counter() - t0
+    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {B * s_q} query tokens (seeded order), fp64 NumPy oracle, "
+                      f"{elapsed:.1f} s wall; host cpu_count={os.cpu_count()}"}
 
 
 def main():
@@ -311,6 +381,9 @@ def main():
                          "step that produces its inputs (GB/s against HBM); or FP8 sparse decode "
                          "(MQA over 656-byte cache rows, TFLOP/s against the bf16 matrix peak; "
                          "workload decode_b128 unless --workload names another decode config)")
+    ap.add_argument("--flushed", action="store_true",
+                    help="prefill only: also time the launches with a 512 MiB buffer written before "
+                         "each (cold caches); reported as kernel_ms_flushed_median")
     ap.add_argument("--splits", default="auto",
                     help="decode only: parts per index list (an integer, or 'auto' for the library's "
                          "choice; 1 is the single-pass kernel)")
@@ -419,6 +492,20 @@ def main():
             e.record(stream)
         torch.cuda.synchronize()
         schedule_ms = round(float(np.mean([s.elapsed_time(e) for s, e in pe])), 4)
+    # the same launches with a 512 MiB buffer written before each (caches flushed)
+    flushed_ms = None
+    if args.flushed:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for s, e in fe:
+            flush.fill_(1)
+            s.record(stream)
+            step()
+            e.record(stream)
+        torch.cuda.synchronize()
+        flushed_ms = round(float(np.median([s.elapsed_time(e) for s, e in fe])), 4)
+        del flush
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
     flop = n_act * FLOP_PER_TILE
     kv_bytes = n_act * (KV_BYTES_PER_TILE + (TILE * 4 if p.quant_type == 1 else 0))
@@ -447,6 +534,7 @@ def main():
         "kernel_ms_min": round(float(kernel_ms.min()), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "schedule_pre_pass_ms": schedule_ms,
+        "kernel_ms_flushed_median": flushed_ms,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": recorded_traffic(p.cfg.name)
