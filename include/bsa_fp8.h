@@ -29,9 +29,10 @@
  * Ownership and threading
  *   Every array argument is a DEVICE pointer owned by the caller.  The library
  *   allocates no memory, never synchronises, and never reads device data on the
- *   host: a call validates its static arguments on the host, then enqueues one
- *   kernel on `stream` (a hipStream_t; NULL = the null stream) and returns.
- *   Results are ready when that stream reaches the kernel.
+ *   host: a call validates its static arguments on the host, then enqueues its
+ *   kernels on `stream` (a hipStream_t; NULL = the null stream) and returns --
+ *   one kernel, except where an entry point below says otherwise.  Results are
+ *   ready when that stream reaches the end of the call's last kernel.
  *
  * Errors
  *   A call returns BSA_OK (0) or a positive bsa_status.  Static-argument errors
@@ -245,7 +246,7 @@ int bsa_fp8_prefill_ex(const void* q, const void* kcache, const void* vcache,
  * entry do not matter and on return are unspecified.  `schedule` is int32
  * [B * Hq * ceil(max_seqlen_q/128)].  block_mask, sparse_indices and
  * sparse_seq_len as for bsa_fp8_prefill_ex (all NULL = dense); `options` may
- * be NULL; only its sparse_indices / sparse_seq_len are read.  Two kernels are
+ * be NULL; only its sparse_indices / sparse_seq_len are read.  Four kernels are
  * enqueued on `stream`.  Errors as for bsa_fp8_prefill_ex, plus
  * BSA_ERR_NULL_POINTER when workspace or schedule is NULL with tasks present.
  */
