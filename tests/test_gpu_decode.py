@@ -72,6 +72,8 @@ SMALL = [
     dict(lkv=(20, 500), s_q=1, h_q=64, topk=5),                # top-k below one block
     dict(lkv=(2048,), s_q=2, h_q=128, topk=2048, page_size=64),
     dict(lkv=(900, 350), s_q=1, h_q=192, topk=300, ragged=True),   # three 64-head groups
+    dict(lkv=(20, 3), s_q=2, h_q=64, topk=1),                  # a single entry per list
+    dict(lkv=(700,), s_q=2, h_q=256, topk=96, page_size=32),   # two 128-head workgroups per token
 ]
 
 

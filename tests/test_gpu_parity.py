@@ -152,6 +152,34 @@ def test_deterministic():
     np.testing.assert_array_equal(l1, l2)
 
 
+def test_widest_mask_and_extra_rows_ignored():
+    """A mask of the widest accepted shape (4096 KV tiles) with three extra
+    Q-tile rows, random bits everywhere outside the tight shape: tiles past a
+    sequence's KV length and rows past its queries select nothing, so the
+    result is the tight mask's, bit for bit."""
+    import dataclasses
+    p = make_problem("tiny", seed=19, **SMALL[1])
+    B, Hq, mt, mkv = p.block_mask.shape
+    rng = np.random.default_rng(19)
+    wide = rng.integers(0, 2, size=(B, Hq, mt + 3, 4096), dtype=np.uint8)
+    wide[:, :, :mt, :mkv] = p.block_mask
+    q = dataclasses.replace(p, block_mask=wide)
+    go, gl = check(p, label="tight mask")
+    say("[gpu] widest mask")
+    wo, wl = run_gpu(q)
+    np.testing.assert_array_equal(go, wo)
+    np.testing.assert_array_equal(gl, wl)
+
+
+def test_sequences_without_queries():
+    """Batch entries with no query tokens (with and without cached keys) next to
+    ordinary ones: they produce no work and do not disturb the others."""
+    p = make_problem("tiny", seed=20, lq=(0, 150, 0, 33), lkv=(300, 260, 0, 33), hq=4, hkv=2,
+                     quant_type=1, kv_layout=1, page_size=32, keep=0.6)
+    check(p, label="sequences without queries")
+    check(p, causal=False, label="sequences without queries, non-causal")
+
+
 FULL = [("dense8k", 40, ()), ("sparse16k", 48, ()), ("varlen", 48, ((3, 5, 17), (0, 0, 0))),
         ("long128k", 64, ((0, 0, 0), (0, 31, 1023), (0, 7, 1)))]
 
