@@ -43,17 +43,22 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def recorded_traffic(workload):
-    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of
-    this exact kernel source, or None when there is no record or the kernel
-    source changed since it was taken."""
+def traffic_record(workload):
+    """The rocprofv3 FETCH_SIZE / WRITE_SIZE record of this exact kernel source
+    for the workload, or None when there is none or the source changed since."""
     try:
         rec = json.load(open(TRAFFIC_FILE))[workload]
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return rec["hbm_bytes_per_launch"]
+    return rec
+
+
+def recorded_traffic(workload):
+    """HBM bytes (read + written) per launch from the record, or None."""
+    rec = traffic_record(workload)
+    return None if rec is None else rec["hbm_bytes_per_launch"]
 
 
 def _counter_means(directory, kernel_substr):
@@ -507,6 +512,11 @@ def main():
         flushed_ms = round(float(np.median([s.elapsed_time(e) for s, e in fe])), 4)
         del flush
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
+    rec = traffic_record(p.cfg.name) if args.form == "mask" and not args.schedule else None
+    dram_read_gbps = None
+    if rec is not None:
+        dram_read_gbps = round(rec["fetch_kib_per_launch"] * 1024 * rec["fetch_scale"]
+                               / (float(np.median(kernel_ms)) / 1e3) / 1e9, 1)
     flop = n_act * FLOP_PER_TILE
     kv_bytes = n_act * (KV_BYTES_PER_TILE + (TILE * 4 if p.quant_type == 1 else 0))
     tflops = flop / (wall / args.steps) / 1e12
@@ -535,6 +545,8 @@ def main():
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "schedule_pre_pass_ms": schedule_ms,
         "kernel_ms_flushed_median": flushed_ms,
+        # HBM read bytes per launch (the FETCH_SIZE record) over the median launch
+        "kv_gbps_dram": dram_read_gbps,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": recorded_traffic(p.cfg.name)
