@@ -307,13 +307,28 @@ def bench_decode(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        # the call captured once and replayed: what a serving loop does to drop launch costs
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s_, e_ in ev:
         s_.record(stream)
-        step()
+        run()
         e_.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -329,7 +344,7 @@ def bench_decode(args):
         "dtype": "bf16 (fp8_e4m3 cache dequantised to bf16, fp32 accumulate)",
         "data": "synthetic (seeded N(0,1); power-of-two tile descales)",
         "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "selected_tokens": int(valid),
-                   "query_tokens": B * s_q, "num_splits": splits},
+                   "query_tokens": B * s_q, "num_splits": splits, "graph": bool(args.graph)},
         "kernel_ms_min": round(float(kernel_ms.min()), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "kv_gbps_logical": round(nbytes / med / 1e9, 1),
@@ -389,6 +404,8 @@ def main():
     ap.add_argument("--flushed", action="store_true",
                     help="prefill only: also time the launches with a 512 MiB buffer written before "
                          "each (cold caches); reported as kernel_ms_flushed_median")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode only: capture the call in a HIP graph and time its replays")
     ap.add_argument("--splits", default="auto",
                     help="decode only: parts per index list (an integer, or 'auto' for the library's "
                          "choice; 1 is the single-pass kernel)")
