@@ -404,7 +404,7 @@ long long bsa_fp8_sparse_decode_workspace_bytes(const bsa_fp8_decode_dims* dims,
  * A part count for bsa_fp8_sparse_decode_ex (host only, no device access): the
  * fewest parts whose row lists fit (at most BSA_DECODE_MAX_TOPK entries each),
  * raised until the decode grid has about 256 workgroups (one per compute
- * unit) but never below 4 blocks of 32 entries per part, capped at
+ * unit) but never below 2 blocks of 32 entries per part, capped at
  * BSA_DECODE_MAX_SPLITS.  1 for NULL dims or dims the decode rejects.
  */
 int bsa_fp8_sparse_decode_num_splits(const bsa_fp8_decode_dims* dims);

@@ -324,12 +324,14 @@ def test_split_decode_sizes(lib):
     assert bsa.bsa_fp8_sparse_decode_workspace_bytes(1, 2, 64, 5) == 5 * 2 * 64 * 513 * 4
     ns = lambda **kw: lib.bsa_fp8_sparse_decode_num_splits(ctypes.byref(dd(**kw)))  # noqa: E731
     # 128 heads are one workgroup per query token; B*s_q = 4 -> 64 parts wanted,
-    # but 2048 entries are 64 blocks, at least 4 per part -> 16
-    assert ns() == 16
+    # but 2048 entries are 64 blocks, at least 2 per part -> 32
+    assert ns() == 32
+    assert ns(batch=8) == 16                         # 16 query tokens x 16 parts = 256 workgroups
     assert ns(batch=128) == 1                        # 256 workgroups already
     assert ns(batch=1, s_q=1, topk=65536) == 256     # 2048 blocks: 256 parts of 8
     assert ns(batch=128, topk=65536) == 8            # the list must fit: 8 parts of 8192
-    assert ns(batch=1, s_q=1, num_heads_q=64, topk=128) == 1
+    assert ns(batch=1, s_q=1, num_heads_q=64, topk=128) == 2   # 4 blocks: 2 parts of 2
+    assert ns(batch=1, s_q=1, num_heads_q=64, topk=32) == 1    # one block cannot be split
     assert ns(num_heads_q=96) == 1 and ns(topk=0) == 1
     assert lib.bsa_fp8_sparse_decode_num_splits(None) == 1
     for kw in (dict(), dict(batch=1, s_q=1, topk=100000), dict(batch=64, topk=30000)):
