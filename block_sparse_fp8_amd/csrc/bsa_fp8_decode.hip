@@ -34,6 +34,12 @@
 //      row-major K tile through the transposing read ds_read_b64_tr_b16.
 // Epilogue: O = O_acc / l per head, bfloat16; LSE = ln sum exp(score).  A
 // query with no valid index gets O = 0 and LSE = -FLT_MAX.
+//
+// Split lists (the article's launch grid also runs over "SM parts"): with
+// num_splits > 1 the part index is the fastest-varying part of the workgroup
+// id, part p walks only its own blocks of the list and stores O_p / l_p in
+// fp32 and its log2-sum-exp in a caller workspace; a second kernel merges the
+// parts of every (query token, head) by weights 2^(lse_p - max).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
