@@ -6,9 +6,10 @@
 // values gets the descale d = amax / 448, optionally rounded up to a power of
 // two, and each value is stored as E4M3(x / d).  Rows whose descale is given
 // (K for quant type 0, V for both types) use it in the same formula.  The
-// divisions are IEEE float32 (correctly rounded), the E4M3 rounding is to
-// nearest even and saturates at 448, so every code and descale is a pure
-// function of the bfloat16 input.
+// descale is an IEEE float32 division and every quotient x / d equals the
+// correctly rounded float32 one (computed from one reciprocal per row, see
+// encode8), the E4M3 rounding is to nearest even and saturates at 448, so
+// every code and descale is a pure function of the bfloat16 input.
 //
 // One row per 16 lanes: each lane loads 8 bfloat16 values (16 bytes), the row
 // maximum is reduced over the 16 lanes with cross-lane shuffles, and each lane
@@ -76,13 +77,35 @@ __device__ __forceinline__ float round_up_pow2(float d) {
 }
 
 // E4M3 codes of fp32(x[i] / d), packed little-endian into two dwords.
+//
+// For descales in [2^-80, 2^100] the quotients come from one reciprocal per
+// row instead of eight divisions: with r = 1/d correctly rounded and
+// q0 = RN(x*r) within an ulp of x/d, the remainder x - q0*d is exact in one
+// fma and RN(q0 + remainder*r) is the correctly rounded x/d (Markstein's
+// theorem for quotients; the range keeps the remainder of every x whose
+// quotient reaches the E4M3 grid clear of underflow).  q0 is first clamped to
+// [-1024, 1024]: a quotient beyond that saturates to 448 whatever its rounding,
+// and the clamp keeps the remainder finite.  The sign is taken from x so that
+// -0 stays -0.  tests/quotient_check.c compares the resulting codes with those
+// of the IEEE quotient for every descale amax/448 and every bfloat16 x.  Other
+// descales use IEEE division per value.
 __device__ __forceinline__ v2i encode8(const float* x, float d) {
   float y[8];
+  if (d >= 0x1p-80f && d <= 0x1p100f) {
+    const float r = 1.0f / d;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = fmaxf(fminf(x[i] / d, kFp8Max), -kFp8Max);
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = __builtin_amdgcn_fmed3f(x[i] * r, -1024.0f, 1024.0f);
+      const float q = fmaf(fmaf(-q0, d, x[i]), r, q0);
+      y[i] = __builtin_amdgcn_fmed3f(copysignf(q, x[i]), -kFp8Max, kFp8Max);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fmaxf(fminf(x[i] / d, kFp8Max), -kFp8Max);
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], __builtin_nondeterministic_value(0), false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], __builtin_nondeterministic_value(0), false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
   return v2i{lo, hi};
 }
