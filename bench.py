@@ -431,8 +431,9 @@ def main():
         ingest_counters(args.workload, *args.ingest_counters, command=args.ingest_command)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the kernel shards by kv-head with no communication; see the design notes)",
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the prefill shards by kv-head: each GPU takes Hkv/N kv-heads with their q-heads "
+              "and needs no communication)",
               file=sys.stderr)
         sys.exit(2)
 
