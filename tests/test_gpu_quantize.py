@@ -102,6 +102,33 @@ def test_quantize_q_only_and_append_only():
     np.testing.assert_array_equal(d["kscale"].cpu().numpy(), want[4])
 
 
+# Given descales on both sides of the range [2^-80, 2^100] in which the kernel
+# forms quotients from one reciprocal per row (outside it, it divides per value),
+# and Q rows whose computed descale amax/448 falls on either side of 2^-80.
+EDGE_DESCALES = [2.0 ** -90, float(np.nextafter(np.float32(2.0 ** -80), np.float32(0))), 2.0 ** -80,
+                 2.0 ** 100, float(np.nextafter(np.float32(2.0 ** 100), np.float32(np.inf))), 2.0 ** 110]
+
+
+@pytest.mark.parametrize("quant_type", [0, 1])
+@pytest.mark.parametrize("dsc", EDGE_DESCALES)
+def test_quantize_descale_range_edges(dsc, quant_type):
+    p = make_problem("tiny", seed=450, **dict(CASES[0], quant_type=quant_type))
+    a = append_inputs(p, seed=45, spread=False)
+    rng = np.random.default_rng(46)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()  # noqa: E731
+    # Q rows scaled by 2^e: computed descales from ~2^-109 to ~2^-60 straddle 2^-80
+    e = rng.choice([-100, -92, -88, -84, -81, -80, -79, -76, -70, -60], size=a["q"].shape[:2])
+    a["q"] = bf(a["q"] * np.exp2(e)[..., None])
+    # K and V rows ~ 64 * N(0,1) * dsc, so their quotients by the given descale span the E4M3 grid
+    a["k"] = bf(a["k"] * 64.0 * dsc)
+    a["v"] = bf(a["v"] * 64.0 * dsc)
+    a["kscale"] = np.array([dsc], np.float32)
+    a["vscale"] = np.full(a["vscale"].shape, dsc, np.float32)
+    say(f"[gpu] quantize descale edge {dsc:.3g} quant {quant_type}")
+    got = run_gpu_quantize(p, a, False)
+    assert_same(got[:5], oracle_quantize(p, a, False))
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["sparse16k", "varlen", "dense8k"])
 def test_full_size_bitwise(name):
