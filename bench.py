@@ -33,31 +33,43 @@ KV_BYTES_PER_TILE = 2 * TILE * TILE             # 32,768
 PEAK_FP8_TFLOPS = 5000.0                        # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0
 METRIC = "effective FP8 TFLOPS (active tiles) + prefill tokens/s; % of FP8 MFMA peak"
-KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_fp8_amd", "csrc", "bsa_fp8_prefill.hip")
+_CSRC = os.path.join(ROOT, "block_sparse_fp8_amd", "csrc")
+# per operation: the kernel source the counters belong to and the kernel's name
+KERNELS = {
+    "prefill": (os.path.join(_CSRC, "bsa_fp8_prefill.hip"), "bsa_fp8_prefill_kernel"),
+    "quantize_append": (os.path.join(_CSRC, "bsa_fp8_quantize.hip"), "bsa_fp8_quantize_kernel"),
+    "decode": (os.path.join(_CSRC, "bsa_fp8_decode.hip"), "bsa_fp8_decode_kernel"),
+}
+KERNEL_SOURCE = KERNELS["prefill"][0]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 * 1024 * 1024   # size of the calibration copy (see --ingest-counters)
 
 
-def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_hash(op="prefill"):
+    with open(KERNELS[op][0], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_record(workload):
+def _traffic_key(workload, op):
+    return workload if op == "prefill" else f"{op}:{workload}"
+
+
+def traffic_record(workload, op="prefill"):
     """The rocprofv3 FETCH_SIZE / WRITE_SIZE record of this exact kernel source
-    for the workload, or None when there is none or the source changed since."""
+    for the operation and workload, or None when there is none or the source
+    changed since."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))[workload]
+        rec = json.load(open(TRAFFIC_FILE))[_traffic_key(workload, op)]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(op):
         return None
     return rec
 
 
-def recorded_traffic(workload):
+def recorded_traffic(workload, op="prefill"):
     """HBM bytes (read + written) per launch from the record, or None."""
-    rec = traffic_record(workload)
+    rec = traffic_record(workload, op)
     return None if rec is None else rec["hbm_bytes_per_launch"]
 
 
@@ -70,16 +82,18 @@ def _counter_means(directory, kernel_substr):
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
-def ingest_counters(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command):
-    """Record FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the prefill kernel,
-    scaled by what the same counters read for a plain copy of COPY_BYTES."""
-    f = _counter_means(fetch_dir, "bsa_fp8_prefill_kernel")["FETCH_SIZE"]
-    w = _counter_means(write_dir, "bsa_fp8_prefill_kernel")["WRITE_SIZE"]
+def ingest_counters(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command, op="prefill"):
+    """Record FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the operation's
+    kernel, scaled by what the same counters read for a plain copy of
+    COPY_BYTES."""
+    kname = KERNELS[op][1]
+    f = _counter_means(fetch_dir, kname)["FETCH_SIZE"]
+    w = _counter_means(write_dir, kname)["WRITE_SIZE"]
     cf = _counter_means(cal_fetch_dir, "copyBuffer")["FETCH_SIZE"]
     cw = _counter_means(cal_write_dir, "copyBuffer")["WRITE_SIZE"]
     fetch_scale = COPY_BYTES / (cf * 1024)
     write_scale = COPY_BYTES / (cw * 1024)
-    rec = {"kernel_source_sha256": kernel_source_hash(),
+    rec = {"kernel_source_sha256": kernel_source_hash(op),
            "fetch_kib_per_launch": f, "write_kib_per_launch": w,
            "fetch_scale": fetch_scale, "write_scale": write_scale,
            "hbm_bytes_per_launch": f * 1024 * fetch_scale + w * 1024 * write_scale,
@@ -88,7 +102,7 @@ def ingest_counters(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir
         allrec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         allrec = {}
-    allrec[workload] = rec
+    allrec[_traffic_key(workload, op)] = rec
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(allrec, fh, indent=1, sort_keys=True)
     print(json.dumps(rec))
@@ -233,7 +247,7 @@ def bench_quantize_append(p, args):
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": {"bound": "hbm", "achieved": round(nbytes / med / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(nbytes / med / 1e9 / PEAK_HBM_GBPS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic(p.cfg.name, "quantize_append")},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_quantize(p, a, args.cpu_budget)
@@ -413,7 +427,8 @@ def main():
                     help="run the scheduling pre-pass inside every step and launch the prefill "
                          "in its task order")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
-                    help="record HBM traffic of --workload from rocprofv3 counter CSV directories and exit")
+                    help="record HBM traffic of --op's kernel on --workload from rocprofv3 counter CSV "
+                         "directories and exit")
     ap.add_argument("--ingest-command", default="", help="command line recorded with --ingest-counters")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB (x3), for calibrating FETCH_SIZE/WRITE_SIZE")
@@ -428,7 +443,7 @@ def main():
         print(json.dumps({"copied_bytes": COPY_BYTES, "copies": 3}))
         return
     if args.ingest_counters:
-        ingest_counters(args.workload, *args.ingest_counters, command=args.ingest_command)
+        ingest_counters(args.workload, *args.ingest_counters, command=args.ingest_command, op=args.op)
         return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
