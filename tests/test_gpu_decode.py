@@ -86,6 +86,27 @@ def test_small_vs_oracle(i):
     say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
 
 
+@pytest.mark.parametrize("frac", [1.0, 0.5])
+def test_descales_not_powers_of_two(frac):
+    """Descales that are not powers of two take the fp32-product path (the
+    power-of-two ones a single scaled conversion).  Multiplying a descale by
+    1.5 keeps code * descale exact in bfloat16 (4 + 2 significant bits), so
+    the bound above still holds; frac 0.5 changes half the (token, tile)
+    descales, so lanes of one wave take different paths."""
+    p = make_decode_problem("decode_tiny", seed=520, **SMALL[0])
+    rng = np.random.default_rng(521)
+    sc = p.kv_cache[..., 512:528].copy().view(np.float32)       # [pages, page_size, 4]
+    pick = rng.random(sc.shape) < frac
+    sc[pick] *= np.float32(1.5)
+    p.kv_cache[..., 512:528] = sc.view(np.uint8)
+    say(f"[gpu] decode descales x1.5 on {frac:.0%} of tiles")
+    go, gl = run_gpu(p)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
+    go2, gl2 = run_gpu(p, num_splits=3)
+    compare(go2, gl2, eo, el, ea)
+
+
 def test_empty_lists_and_sequences():
     p = make_decode_problem("decode_tiny", seed=510, lkv=(300, 0, 90), s_q=2, h_q=64, topk=40)
     p.indices[0, 1, :] = -1                          # nothing selected
