@@ -298,7 +298,8 @@ def bench_decode(args):
     p = make_decode_problem(name)
     d = p.to_device("cuda")
     B, s_q, h_q, _ = p.q.shape
-    valid = ((p.indices >= 0) & (p.indices < p.seqlens_kv[:, None, None])).sum()
+    n_rows = p.kv_cache.shape[0] * p.kv_cache.shape[1]
+    valid = ((p.indices >= 0) & (p.indices < n_rows)).sum()
     flop = float(valid) * h_q * 2 * (576 + 512)
     nbytes = float(valid) * 656 + B * s_q * h_q * (576 * 2 + 512 * 2)
     out = torch.empty((B, s_q, h_q, 512), dtype=torch.bfloat16, device="cuda")
@@ -311,11 +312,10 @@ def bench_decode(args):
 
     def step():
         if splits == 1:
-            bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"], d["seqlens_kv"],
-                                      softmax_scale=p.softmax_scale, out=out, lse=lse)
+            bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], softmax_scale=p.softmax_scale,
+                                      out=out, lse=lse)
         else:
-            bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], d["block_table"],
-                                         d["seqlens_kv"], num_splits=splits, workspace=ws,
+            bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], num_splits=splits, workspace=ws,
                                          softmax_scale=p.softmax_scale, out=out, lse=lse)
 
     for _ in range(args.warmup):
@@ -386,10 +386,9 @@ def cpu_baseline_decode(p, budget_s):
     t0 = time.perf_counter()
     for i in order:
         b, s = divmod(int(i), s_q)
-        D.sparse_decode(p.q[b:b + 1, s:s + 1], p.kv_cache, p.indices[b:b + 1, s:s + 1],
-                        p.block_table[b:b + 1], p.seqlens_kv[b:b + 1], p.softmax_scale)
+        D.sparse_decode(p.q[b:b + 1, s:s + 1], p.kv_cache, p.indices[b:b + 1, s:s + 1], p.softmax_scale)
         idx = p.indices[b, s]
-        flop += float(((idx >= 0) & (idx < p.seqlens_kv[b])).sum()) * h_q * 2 * (576 + 512)
+        flop += float(D.valid_entries(idx, p.kv_cache).size) * h_q * 2 * (576 + 512)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break

@@ -112,7 +112,6 @@ class DecodeDims(ctypes.Structure):
         ("topk", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
-        ("max_pages_per_seq", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
     ]
 
@@ -145,9 +144,9 @@ def load_library():
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(Dims),
                                             vp, vp, vp, vp, vp, vp]
     lib.bsa_fp8_quantize_append.restype = ctypes.c_int
-    lib.bsa_fp8_sparse_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DecodeDims), vp, vp, vp]
+    lib.bsa_fp8_sparse_decode.argtypes = [vp, vp, vp, ctypes.POINTER(DecodeDims), vp, vp, vp]
     lib.bsa_fp8_sparse_decode.restype = ctypes.c_int
-    lib.bsa_fp8_sparse_decode_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DecodeDims),
+    lib.bsa_fp8_sparse_decode_ex.argtypes = [vp, vp, vp, ctypes.POINTER(DecodeDims),
                                              ctypes.c_int, vp, vp, vp, vp]
     lib.bsa_fp8_sparse_decode_ex.restype = ctypes.c_int
     lib.bsa_fp8_sparse_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeDims), ctypes.c_int]
@@ -430,11 +429,9 @@ def bsa_fp8_quantize_append(q_in, k_in, v_in, cu_seqlens_q, seqlens_kv, block_ta
     return q_out, qscale_out
 
 
-def _decode_dims(batch, s_q, num_heads_q, topk, num_pages=0, page_size=64, max_pages_per_seq=0,
-                 softmax_scale=1.0):
+def _decode_dims(batch, s_q, num_heads_q, topk, num_pages=0, page_size=64, softmax_scale=1.0):
     return DecodeDims(batch=batch, s_q=s_q, num_heads_q=num_heads_q, topk=topk, num_pages=num_pages,
-                      page_size=page_size, max_pages_per_seq=max_pages_per_seq,
-                      softmax_scale=float(softmax_scale))
+                      page_size=page_size, softmax_scale=float(softmax_scale))
 
 
 def bsa_fp8_sparse_decode_workspace_bytes(batch, s_q, num_heads_q, num_splits):
@@ -454,15 +451,14 @@ def bsa_fp8_sparse_decode_num_splits(batch, s_q, num_heads_q, topk):
         ctypes.byref(_decode_dims(batch, s_q, num_heads_q, topk)))
 
 
-def _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, out, lse,
-                   return_lse, stream, num_splits, workspace):
+def _sparse_decode(q, kv_cache, indices, softmax_scale, out, lse, return_lse, stream, num_splits,
+                   workspace):
     device = q.device
     if device.type != "cuda":
         raise ValueError("bsa_fp8_sparse_decode runs on a GPU; q is on " + str(device))
     _check("q", q, (torch.bfloat16,), device)
     _check("kv_cache", kv_cache, (torch.uint8,), device)
-    for name, t in (("indices", indices), ("block_table", block_table), ("seqlens_kv", seqlens_kv)):
-        _check(name, t, (torch.int32,), device)
+    _check("indices", indices, (torch.int32,), device)
     if q.dim() != 4 or q.shape[3] != 576:
         raise ValueError("q must be [B, s_q, h_q, 576]")
     if kv_cache.shape[-1] != 656 or kv_cache.dim() not in (3, 4) or \
@@ -481,15 +477,14 @@ def _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale,
         lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=device)
     elif lse is not None:
         _check("lse", lse, (torch.float32,), device)
-    dims = _decode_dims(B, s_q, h_q, indices.shape[2], kv_cache.shape[0], kv_cache.shape[1],
-                        block_table.shape[1], softmax_scale)
+    dims = _decode_dims(B, s_q, h_q, indices.shape[2], kv_cache.shape[0], kv_cache.shape[1], softmax_scale)
     if stream is None:
         stream = torch.cuda.current_stream(device).cuda_stream
     lib = load_library()
     if num_splits is None:
         status = lib.bsa_fp8_sparse_decode(
-            _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(block_table), _ptr(seqlens_kv),
-            ctypes.byref(dims), _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
+            _ptr(q), _ptr(kv_cache), _ptr(indices), ctypes.byref(dims), _ptr(out), _ptr(lse),
+            ctypes.c_void_p(stream))
     else:
         if num_splits == "auto":
             num_splits = lib.bsa_fp8_sparse_decode_num_splits(ctypes.byref(dims))
@@ -503,34 +498,31 @@ def _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale,
             if workspace.numel() < need:
                 raise ValueError(f"workspace holds {workspace.numel()} bytes; {need} are needed")
         status = lib.bsa_fp8_sparse_decode_ex(
-            _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(block_table), _ptr(seqlens_kv),
-            ctypes.byref(dims), int(num_splits), _ptr(workspace), _ptr(out), _ptr(lse),
-            ctypes.c_void_p(stream))
+            _ptr(q), _ptr(kv_cache), _ptr(indices), ctypes.byref(dims), int(num_splits), _ptr(workspace),
+            _ptr(out), _ptr(lse), ctypes.c_void_p(stream))
     if status != 0:
         raise BsaError(status, status_string(status))
     return out, lse
 
 
-def bsa_fp8_sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, *, softmax_scale=None,
-                          out=None, lse=None, return_lse=True, stream=None):
+def bsa_fp8_sparse_decode(q, kv_cache, indices, *, softmax_scale=None, out=None, lse=None,
+                          return_lse=True, stream=None):
     """Call the C entry point of the same name: FP8 sparse decode (MQA over a
     paged cache of 656-byte token rows).  q bf16 [B, s_q, h_q, 576]; kv_cache
     uint8 [num_pages, page_size, 656] (or with a kv-head axis of 1); indices
-    int32 [B, s_q, topk]; block_table int32 [B, max_pages]; seqlens_kv int32
-    [B].  Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, h_q, s_q])."""
-    return _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, out, lse,
-                          return_lse, stream, None, None)
+    int32 [B, s_q, topk] of cache rows (page * page_size + slot, -1 unused).
+    Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, h_q, s_q])."""
+    return _sparse_decode(q, kv_cache, indices, softmax_scale, out, lse, return_lse, stream, None, None)
 
 
-def bsa_fp8_sparse_decode_ex(q, kv_cache, indices, block_table, seqlens_kv, *, num_splits="auto",
-                             workspace=None, softmax_scale=None, out=None, lse=None, return_lse=True,
-                             stream=None):
+def bsa_fp8_sparse_decode_ex(q, kv_cache, indices, *, num_splits="auto", workspace=None,
+                             softmax_scale=None, out=None, lse=None, return_lse=True, stream=None):
     """Call the C entry point of the same name: the sparse decode with each
     index list cut into num_splits parts ("auto": the library's choice) and
     merged.  workspace: a uint8 device tensor of at least
     bsa_fp8_sparse_decode_workspace_bytes bytes, allocated here when None."""
-    return _sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, out, lse,
-                          return_lse, stream, num_splits, workspace)
+    return _sparse_decode(q, kv_cache, indices, softmax_scale, out, lse, return_lse, stream, num_splits,
+                          workspace)
 
 
 def attention_with_kvcache_blocksparse_prefill_fp8(

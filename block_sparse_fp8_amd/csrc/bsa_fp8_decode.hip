@@ -4,7 +4,9 @@
 // attention (every query head reads the same single KV head) with 576-dim keys
 // (512 E4M3 values in four 1x128 tiles with one float32 descale each, then 64
 // bfloat16 values) and 512-dim values (the first 512 key dimensions); each
-// query token attends to its own list of top-k token positions.  The article's
+// query token attends to its own list of top-k cache rows, each named as
+// page-block index * page_block_size + offset in the block, -1 for an unused
+// entry (the article's quick-reproduce paragraph).  The article's
 // kernel dequantises K/V to bfloat16 and runs both products on bfloat16 matrix
 // units; the same split holds here.  Its two thread blocks per query token
 // each dequantise half of the rows and exchange them; here one workgroup
@@ -12,9 +14,9 @@
 // read and dequantised once.
 //
 // Per workgroup (sequence b, query token s, 16*NW heads):
-//   prologue: the cache row of every list entry (page * page_size + slot, or
-//      -1 for an entry outside [0, Lkv)) goes to an LDS list, and Q of each
-//      wave's 16 heads to registers.
+//   prologue: every list entry goes to an LDS list (-1 for an entry that
+//      names no row: negative, or at or past num_pages * page_size), and Q of
+//      each wave's 16 heads to registers.
 //   The list is then walked 32 tokens at a time; the rows of block n+2 are
 //   fetched while block n is computed, by direct-to-LDS loads into a ring of
 //   three staging buffers (41 chunks of 16 bytes per row, spread over 16
@@ -74,12 +76,11 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 struct DecodeParams {
   const uint16_t* q;          // bf16 [B, s_q, h_q, 576]
   const uint8_t* kv;          // [num_pages, page_size, 656]
-  const int32_t* indices;     // [B, s_q, topk]
-  const int32_t* block_table; // [B, max_pages]
-  const int32_t* seqlens_kv;  // [B]
+  const int32_t* indices;     // [B, s_q, topk] cache rows (page * page_size + slot)
   uint16_t* out;              // bf16 [B, s_q, h_q, 512]
   float* lse;                 // [B, h_q, s_q] or nullptr
-  int B, s_q, h_q, topk, page_size, page_shift, max_pages;
+  int B, s_q, h_q, topk;
+  int num_rows;               // num_pages * page_size: entries in [0, num_rows) name a row
   float score_scale;          // softmax_scale * log2(e)
   int num_splits;             // parts of each index list handled by separate workgroups
   int blocks_per_split;       // 32-token blocks per part
@@ -162,10 +163,9 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   const int b = bs / p.s_q;
   const int s = bs - b * p.s_q;
   const int h0 = hg * kHeads;
-  const int lkv = p.seqlens_kv[b];
-  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
   // this workgroup's part of the list: blocks n_begin .. n_begin + nblocks - 1
-  const int nblocks_all = lkv > 0 ? (p.topk + kBlock - 1) / kBlock : 0;
+  // (none when the cache has no rows: no entry can name one)
+  const int nblocks_all = p.num_rows > 0 ? (p.topk + kBlock - 1) / kBlock : 0;
   const int n_begin = split * p.blocks_per_split;
   const int nblocks = max(0, min(nblocks_all - n_begin, p.blocks_per_split));
 
@@ -185,8 +185,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
     const int avail = p.topk - n_begin * kBlock;  // entries of the list from this part on
     for (int k = tid; k < nblocks * kBlock; k += kThreads) {  // padded to whole blocks with -1
       const int idx = k < avail ? idx_row[k] : -1;
-      const bool ok = idx >= 0 && idx < lkv;
-      rows_lds[k] = ok ? bt[idx >> p.page_shift] * p.page_size + (idx & (p.page_size - 1)) : -1;
+      rows_lds[k] = idx >= 0 && idx < p.num_rows ? idx : -1;
     }
   }
   __syncthreads();
@@ -195,7 +194,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   // with 8 lanes per token each lane does the work of parts 2*part, 2*part+1)
   const int tok = tid / kTokThreads;
   const int part = tid % kTokThreads;
-  const int fallback_row = lkv > 0 ? bt[0] * p.page_size : 0;  // position 0: always readable
+  const int fallback_row = 0;  // loads of unused entries read row 0 (exists whenever nblocks > 0)
   auto row_of = [&](int n) -> int { return n < nblocks ? rows_lds[n * kBlock + tok] : -1; };
   const uint32_t stage_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage_lds) + wave * kWaveStage;
   // Issue the loads of block n into staging buffer n % 3: the same number of
@@ -527,28 +526,25 @@ long long bsa_fp8_sparse_decode_workspace_bytes(const bsa_fp8_decode_dims* dims,
 
 
 int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t* indices,
-                             const int32_t* block_table, const int32_t* seqlens_kv,
                              const bsa_fp8_decode_dims* dims, int num_splits, void* workspace, void* out,
                              float* lse, void* stream) {
   if (dims == nullptr) return BSA_ERR_NULL_POINTER;
   const bsa_fp8_decode_dims d = *dims;
-  if (d.batch < 0 || d.s_q < 0 || d.num_heads_q <= 0 || d.topk <= 0 || d.num_pages < 0 ||
-      d.max_pages_per_seq < 0)
-    return BSA_ERR_SIZE;
+  if (d.batch < 0 || d.s_q < 0 || d.num_heads_q <= 0 || d.topk <= 0 || d.num_pages < 0) return BSA_ERR_SIZE;
   if (d.num_heads_q % 64 != 0) return BSA_ERR_GQA;
   if (num_splits < 1 || num_splits > kMaxSplits) return BSA_ERR_SIZE;
   const int nblocks_all = (d.topk + kBlock - 1) / kBlock;
   const int bps = (nblocks_all + num_splits - 1) / num_splits;
   if ((int64_t)bps * kBlock > kMaxTopk) return BSA_ERR_TOO_LARGE;  // a part's row list must fit in LDS
-  if (d.page_size != 32 && d.page_size != 64) return BSA_ERR_PAGE_SIZE;
+  if (d.page_size <= 0) return BSA_ERR_PAGE_SIZE;
   if (!bsa::finite_float(d.softmax_scale)) return BSA_ERR_SOFTMAX_SCALE;
   const int nw = d.num_heads_q % 128 == 0 ? 8 : 4;  // 16 heads per wave
   const int64_t grid = (int64_t)d.batch * d.s_q * (d.num_heads_q / (16 * nw)) * num_splits;
   if (grid > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
   if ((int64_t)d.num_pages * d.page_size > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;  // 32-bit row ids
   if (grid == 0) return BSA_OK;
-  if (q == nullptr || kv_cache == nullptr || indices == nullptr || block_table == nullptr ||
-      seqlens_kv == nullptr || out == nullptr || (num_splits > 1 && workspace == nullptr))
+  if (q == nullptr || kv_cache == nullptr || indices == nullptr || out == nullptr ||
+      (num_splits > 1 && workspace == nullptr))
     return BSA_ERR_NULL_POINTER;
   if (num_splits > 1 && partial_rows(d) > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
   if (num_splits > 1 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return BSA_ERR_SIZE;
@@ -557,17 +553,13 @@ int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t*
   p.q = static_cast<const uint16_t*>(q);
   p.kv = static_cast<const uint8_t*>(kv_cache);
   p.indices = indices;
-  p.block_table = block_table;
-  p.seqlens_kv = seqlens_kv;
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   p.B = d.batch;
   p.s_q = d.s_q;
   p.h_q = d.num_heads_q;
   p.topk = d.topk;
-  p.page_size = d.page_size;
-  p.page_shift = d.page_size == 64 ? 6 : 5;
-  p.max_pages = d.max_pages_per_seq;
+  p.num_rows = d.num_pages * d.page_size;
   p.score_scale = d.softmax_scale * kLog2e;
   p.num_splits = num_splits;
   p.blocks_per_split = bps;
@@ -587,10 +579,8 @@ int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t*
 }
 
 int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* indices,
-                          const int32_t* block_table, const int32_t* seqlens_kv,
                           const bsa_fp8_decode_dims* dims, void* out, float* lse, void* stream) {
-  return bsa_fp8_sparse_decode_ex(q, kv_cache, indices, block_table, seqlens_kv, dims, 1, nullptr, out, lse,
-                                  stream);
+  return bsa_fp8_sparse_decode_ex(q, kv_cache, indices, dims, 1, nullptr, out, lse, stream);
 }
 
 }  // extern "C"

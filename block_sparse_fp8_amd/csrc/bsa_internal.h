@@ -68,7 +68,10 @@ inline int resolve(const bsa_fp8_dims* dims, const uint8_t* block_mask, const bs
   if (d.num_heads_kv > 65536) return BSA_ERR_TOO_LARGE;  // page offsets are 32-bit
   const int group = d.num_heads_q / d.num_heads_kv;
   if (group < 1 || group > 16) return BSA_ERR_GQA;
-  if (!finite_float(d.softmax_scale)) return BSA_ERR_SOFTMAX_SCALE;
+  // The kernels keep the score constant strictly positive (a masked score of
+  // -inf must turn into a probability of exactly 0), so a negative scale is
+  // refused rather than silently clamped; 0 gives uniform weights.
+  if (!finite_float(d.softmax_scale) || d.softmax_scale < 0.0f) return BSA_ERR_SOFTMAX_SCALE;
   if (d.causal != 0 && d.causal != 1) return BSA_ERR_SIZE;
 
   bsa_fp8_options o;

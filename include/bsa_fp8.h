@@ -73,14 +73,15 @@ typedef enum {
     BSA_OK = 0,
     BSA_ERR_NULL_POINTER = 1,  /* a required pointer (or dims) is NULL          */
     BSA_ERR_HEAD_DIM = 2,      /* head_dim != 128                               */
-    BSA_ERR_PAGE_SIZE = 3,     /* page_size not 32 or 64                        */
+    BSA_ERR_PAGE_SIZE = 3,     /* page_size not 32 or 64 (decode: below 1)      */
     BSA_ERR_GQA = 4,           /* Hq % Hkv != 0 or Hq/Hkv outside 1..16         */
     BSA_ERR_QUANT_TYPE = 5,    /* quant_type not a bsa_quant_type               */
     BSA_ERR_KV_LAYOUT = 6,     /* kv_layout not a bsa_kv_layout                 */
     BSA_ERR_SIZE = 7,          /* a size is negative or inconsistent            */
     BSA_ERR_MASK_SHAPE = 8,    /* mask_tiles_q * 128 < max_seqlen_q, or a mask
                                   dimension is not positive                     */
-    BSA_ERR_SOFTMAX_SCALE = 9, /* softmax_scale not finite                      */
+    BSA_ERR_SOFTMAX_SCALE = 9, /* softmax_scale not finite; for the prefill and
+                                  the schedule also negative                    */
     BSA_ERR_TOO_LARGE = 10,    /* mask_tiles_kv above BSA_MAX_KV_TILES, or a
                                   grid dimension overflow                       */
     BSA_ERR_LAUNCH = 11,       /* the kernel launch failed                      */
@@ -122,7 +123,8 @@ typedef struct {
     int32_t mask_tiles_kv;     /* block_mask dim 3 (KV tiles, Kb)              */
     int32_t kv_layout;         /* bsa_kv_layout                                 */
     int32_t causal;            /* 1: bottom-right causal; 0: no causal mask    */
-    float softmax_scale;       /* usually 1/sqrt(128)                           */
+    float softmax_scale;       /* >= 0 and finite, usually 1/sqrt(128); 0 gives
+                                  uniform weights over each query's keys       */
 } bsa_fp8_dims;
 
 /*
@@ -307,20 +309,27 @@ int bsa_fp8_quantize_append(const void* q_in, const void* k_in, const void* v_in
  * cache row (one token) is 656 bytes: 512 E4M3 codes (key dims 0..511, four
  * 1x128 tiles), 4 float32 descales (one per tile), 64 bfloat16 values (key
  * dims 512..575).  Dequantised key k^ = code * descale (dims 0..511) and the
- * bfloat16 values (dims 512..575); the value is v^ = k^[0..511].  For query
- * token (b, s) and head h:
- *   Omega   = the entries of indices[b, s, :] inside [0, Lkv_b) (an entry
- *             outside selects nothing; an entry listed twice counts twice)
+ * bfloat16 values (dims 512..575); the value is v^ = k^[0..511].  Each entry of
+ * an index list names one cache row as page-block index * page_size + offset
+ * within the block, and -1 marks an unused entry (the article's
+ * quick-reproduce paragraph: indices of shape (batch, seq_len_q, topk) passed
+ * as indices_in_kvcache).  Entry e is therefore the row at page e / page_size,
+ * slot e % page_size.  For query token (b, s) and head h:
+ *   Omega   = the entries of indices[b, s, :] inside [0, num_pages * page_size)
+ *             (any other entry, -1 included, selects nothing; an entry listed
+ *             twice counts twice)
  *   score_j = softmax_scale * q[b, s, h, :] . k^_j      (576 dims)
  *   out[b, s, h, :] = sum_{j in Omega} softmax_j(score) v^_j
  *   lse[b, h, s]    = ln sum_{j in Omega} exp(score_j)
  * An empty Omega gives out = 0 and lse = -FLT_MAX ("Quant Block Sparse
  * Attention", "Sparse indices & PA page table": the empty-task convention).
- * Token position j of sequence b is the row at page block_table[b, j /
- * page_size], slot j % page_size.  Dequantised values are rounded to bfloat16
- * and P to bfloat16 before the bfloat16 matrix products, as the article's
- * kernel does; with power-of-two descales (its reference quantiser) the
- * dequantisation is exact.
+ * No block table or sequence length enters: the lists address cache rows
+ * directly, so a caller that tracks token positions converts them with its
+ * own block table (row = block_table[b][pos / page_size] * page_size +
+ * pos % page_size).  Dequantised values are rounded to bfloat16 and P to
+ * bfloat16 before the bfloat16 matrix products, as the article's kernel does;
+ * with power-of-two descales (its reference quantiser) the dequantisation is
+ * exact.
  */
 typedef struct {
     int32_t batch;             /* B                                             */
@@ -328,32 +337,27 @@ typedef struct {
     int32_t num_heads_q;       /* h_q, a multiple of 64                         */
     int32_t topk;              /* entries per index list, >= 1                  */
     int32_t num_pages;         /* pages of kv_cache                             */
-    int32_t page_size;         /* 32 or 64                                      */
-    int32_t max_pages_per_seq; /* row length of block_table                     */
+    int32_t page_size;         /* slots per page, >= 1                          */
     float softmax_scale;       /* finite                                        */
 } bsa_fp8_decode_dims;
 
 /*
  * q           bf16 [B, s_q, h_q, 576]
  * kv_cache    uint8 [num_pages, page_size, 656]
- * indices     int32 [B, s_q, topk], token positions (any order)
- * block_table int32 [B, max_pages_per_seq]; entries of pages that hold
- *             positions < Lkv_b must be valid page ids (the first is read
- *             whenever Lkv_b > 0)
- * seqlens_kv  int32 [B], Lkv_b
+ * indices     int32 [B, s_q, topk], cache rows page * page_size + slot (any
+ *             order; -1 = unused)
  * out         bf16 [B, s_q, h_q, 512]; lse float [B, h_q, s_q] or NULL
  * Device pointers owned by the caller; one kernel on `stream`; nothing is
  * allocated.  Errors: BSA_ERR_NULL_POINTER, BSA_ERR_SIZE (negative sizes,
- * topk < 1), BSA_ERR_GQA (h_q not a multiple of 64), BSA_ERR_PAGE_SIZE,
- * BSA_ERR_SOFTMAX_SCALE, BSA_ERR_TOO_LARGE (topk above BSA_DECODE_MAX_TOPK,
- * grid or row ids past 2^31), BSA_ERR_LAUNCH.  Rows the index lists do not
- * select are never read, so they may hold anything.  Equivalent to
- * bsa_fp8_sparse_decode_ex with num_splits = 1.
+ * topk < 1), BSA_ERR_GQA (h_q not a multiple of 64), BSA_ERR_PAGE_SIZE
+ * (page_size < 1), BSA_ERR_SOFTMAX_SCALE (not finite), BSA_ERR_TOO_LARGE
+ * (topk above BSA_DECODE_MAX_TOPK, grid or num_pages * page_size past 2^31),
+ * BSA_ERR_LAUNCH.  Rows no entry names are never read, so they may hold
+ * anything.  Equivalent to bsa_fp8_sparse_decode_ex with num_splits = 1.
  */
 #define BSA_DECODE_MAX_TOPK 8192   /* longest index list one workgroup holds      */
 #define BSA_DECODE_MAX_SPLITS 256
 int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* indices,
-                          const int32_t* block_table, const int32_t* seqlens_kv,
                           const bsa_fp8_decode_dims* dims, void* out, float* lse, void* stream);
 
 /*
@@ -389,7 +393,6 @@ int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* in
  * or B * s_q * h_q past 2^31 with num_splits > 1).
  */
 int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t* indices,
-                             const int32_t* block_table, const int32_t* seqlens_kv,
                              const bsa_fp8_decode_dims* dims, int num_splits, void* workspace,
                              void* out, float* lse, void* stream);
 
@@ -412,7 +415,7 @@ int bsa_fp8_sparse_decode_num_splits(const bsa_fp8_decode_dims* dims);
 /* Static text for a bsa_status value (never NULL). */
 const char* bsa_fp8_status_string(int status);
 
-/* Library ABI version, currently 3. */
+/* Library ABI version, currently 4. */
 int bsa_fp8_abi_version(void);
 
 #ifdef __cplusplus

@@ -14,18 +14,23 @@ and its MQA description of the decode step):
   * dequantised key k^ = (code * descale of its tile) for the first 512
     dimensions, the bfloat16 values for the last 64; v^ = k^[:512];
   * for query token (b, s) and head h, the attended set is the list
-    indices[b, s, :] of token positions; an entry outside [0, Lkv_b) is
-    skipped, and an entry listed twice counts twice (a plain reading: each
-    entry is one term of the sum);
+    indices[b, s, :]; each entry names one cache row as page-block index *
+    page_block_size + offset within the block, and -1 marks an unused entry
+    (the article's quick-reproduce paragraph: indices of shape (batch,
+    seq_len_q, topk) passed as indices_in_kvcache).  So entry e is the row
+    kv_cache[e // page_size, e % page_size]; an entry outside
+    [0, num_pages * page_size) selects nothing (the plain reading of "-1 is
+    invalid", extended to every entry that names no row), and an entry listed
+    twice counts twice (each entry is one term of the sum);
   * score_j = softmax_scale * q[b, s, h, :] . k^_j (576 dimensions);
     O = sum_j softmax_j(score) v^_j; LSE = ln sum_j exp(score_j);
   * an empty set gives O = 0 and LSE = -FLT_MAX (the convention of "Quant
     Block Sparse Attention", "Sparse indices & PA page table", for an empty
     sparse task).
 
-Readings where the article leaves a step open: a token position j of sequence
-b lives in page block_table[b, j // page_size], slot j % page_size (the paged
-cache of the prefill); the LSE is laid out [B, h_q, s_q].
+Reading where the article leaves a step open: the LSE is laid out
+[B, h_q, s_q].  No block table and no sequence length enter the decode: the
+index list addresses cache rows directly.
 """
 import numpy as np
 import torch
@@ -51,18 +56,26 @@ def dequant_rows(rows):
     return np.concatenate([nope, rope], axis=-1)
 
 
-def gather_rows(kv_cache, block_table, b, positions):
-    """Cache rows of sequence b at logical token positions (all valid)."""
+def gather_rows(kv_cache, entries):
+    """Cache rows named by index entries (all valid): entry e is the row at
+    page e // page_size, slot e % page_size."""
     page_size = kv_cache.shape[1]
-    pages = np.asarray(block_table[b])[positions // page_size]
-    return kv_cache[pages, positions % page_size].reshape(len(positions), ROW_BYTES)
+    entries = np.asarray(entries, dtype=np.int64)
+    return kv_cache[entries // page_size, entries % page_size].reshape(len(entries), ROW_BYTES)
 
 
-def sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, with_abs=False):
+def valid_entries(idx, kv_cache):
+    """The entries of one index list that name a cache row, in list order."""
+    idx = np.asarray(idx, dtype=np.int64)
+    rows = kv_cache.shape[0] * kv_cache.shape[1]
+    return idx[(idx >= 0) & (idx < rows)]
+
+
+def sparse_decode(q, kv_cache, indices, softmax_scale, with_abs=False):
     """q: float [B, s_q, h_q, 576] (bfloat16 values); kv_cache: uint8
     [num_pages, page_size, 656] (or [num_pages, page_size, 1, 656]);
-    indices: int [B, s_q, topk]; block_table: int [B, max_pages];
-    seqlens_kv: int [B].  Returns (O float64 [B, s_q, h_q, 512],
+    indices: int [B, s_q, topk] of cache rows (page * page_size + slot, -1
+    unused).  Returns (O float64 [B, s_q, h_q, 512],
     LSE float64 [B, h_q, s_q]); with with_abs, also
     A = sum_j softmax_j |v^_j| (same shape as O), the scale of the error that
     rounding each probability by a relative amount causes in O."""
@@ -74,13 +87,11 @@ def sparse_decode(q, kv_cache, indices, block_table, seqlens_kv, softmax_scale, 
     absw = np.zeros((B, s_q, h_q, D_NOPE))
     lse = np.full((B, h_q, s_q), NEG_FLT_MAX)
     for b in range(B):
-        lkv = int(seqlens_kv[b])
         for s in range(s_q):
-            idx = np.asarray(indices[b, s], dtype=np.int64)
-            idx = idx[(idx >= 0) & (idx < lkv)]
+            idx = valid_entries(indices[b, s], kv_cache)
             if idx.size == 0:
                 continue
-            k = dequant_rows(gather_rows(kv_cache, block_table, b, idx))      # [n, 576]
+            k = dequant_rows(gather_rows(kv_cache, idx))                      # [n, 576]
             scores = softmax_scale * (q[b, s] @ k.T)                          # [h, n]
             mx = scores.max(axis=1, keepdims=True)
             w = np.exp(scores - mx)

@@ -10,9 +10,15 @@ rounded to bfloat16.  Pages: sum_b ceil(Lkv_b/page_size) + 3 spare pages in a
 random permutation; block-table entries past a sequence's pages point at a
 spare page; slots past Lkv hold `fill` (random bytes, or NaN codes and NaN
 descales; drawn from a separate generator).  Indices: for each query token, `topk` distinct positions drawn
-uniformly from [0, Lkv_b) (all of them when Lkv_b < topk) in random order; with
-`ragged`, a random tail of each list is set to -1, and a few entries point past
-Lkv_b.  Only random draws, layout and torch's casts happen here.
+uniformly from [0, Lkv_b) (all of them when Lkv_b < topk) in random order, each
+written as the cache row that holds it, page * page_size + slot with page =
+block_table[b, pos // page_size] and slot = pos % page_size (the encoding of
+the FlashMLA FP8 sparse decoding article's quick-reproduce paragraph); with
+`ragged`, a random tail of each list is set to -1, and a few entries are
+other values that name no row (negative, or at or past num_pages *
+page_size).  The block table and sequence lengths only describe how the cache
+was filled; the decode itself reads the rows the indices name.  Only random
+draws, layout and torch's casts happen here.
 """
 from dataclasses import dataclass
 from typing import Tuple
@@ -62,13 +68,17 @@ class DecodeProblem:
 
     def oracle_kwargs(self):
         return dict(q=self.q, kv_cache=self.kv_cache, indices=self.indices,
-                    block_table=self.block_table, seqlens_kv=self.seqlens_kv,
                     softmax_scale=self.softmax_scale)
 
     def to_device(self, device="cuda"):
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
-        return dict(q=t(self.q).to(torch.bfloat16), kv_cache=t(self.kv_cache), indices=t(self.indices),
-                    block_table=t(self.block_table), seqlens_kv=t(self.seqlens_kv))
+        return dict(q=t(self.q).to(torch.bfloat16), kv_cache=t(self.kv_cache), indices=t(self.indices))
+
+    def row_of(self, b, pos):
+        """Cache row (page * page_size + slot) holding token position pos of
+        sequence b."""
+        ps = self.kv_cache.shape[1]
+        return int(self.block_table[b, pos // ps]) * ps + pos % ps
 
 
 def _bf16(x):
@@ -121,16 +131,21 @@ def make_decode_problem(cfg, seed=None, fill="random", lkv=None, s_q=None, h_q=N
             n = min(ps, cfg.lkv[b] - i * ps)
             kv_cache[pg, :n] = rows[used + i, :n]
         used += n_pages_seq[b]
+    n_rows = total_pages * ps
     indices = np.full((B, cfg.s_q, cfg.topk), -1, dtype=np.int32)
     for b in range(B):
         for s in range(cfg.s_q):
             take = min(cfg.topk, cfg.lkv[b])
-            sel = rng.permutation(cfg.lkv[b])[:take].astype(np.int32)
+            pos = rng.permutation(cfg.lkv[b])[:take].astype(np.int64)
+            sel = (block_table[b, pos // ps].astype(np.int64) * ps + pos % ps).astype(np.int32)
             if cfg.ragged:
                 keep = int(rng.integers(take // 2, take + 1))
                 sel = sel[:keep]
-                bad = rng.random(sel.size) < 0.02
-                sel[bad] = cfg.lkv[b] + rng.integers(0, 50, size=int(bad.sum()))
+                bad = np.flatnonzero(rng.random(sel.size) < 0.02)
+                # entries that name no row: past the cache, or negative other than -1
+                junk = np.where(rng.random(bad.size) < 0.5, n_rows + rng.integers(0, 50, size=bad.size),
+                                -2 - rng.integers(0, 1000, size=bad.size))
+                sel[bad] = junk
             indices[b, s, :sel.size] = sel
     return DecodeProblem(cfg=cfg, q=q, kv_cache=kv_cache, indices=indices, block_table=block_table,
                          seqlens_kv=np.asarray(cfg.lkv, dtype=np.int32),

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
     assert "bsa_fp8_prefill" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.bsa_fp8_abi_version() == 3
+    assert lib.bsa_fp8_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -84,6 +84,8 @@ CASES = [
     ("BSA_ERR_MASK_SHAPE", dict(mask_tiles_kv=0), {}),
     ("BSA_ERR_SOFTMAX_SCALE", dict(softmax_scale=float("nan")), {}),
     ("BSA_ERR_SOFTMAX_SCALE", dict(softmax_scale=float("inf")), {}),
+    ("BSA_ERR_SOFTMAX_SCALE", dict(softmax_scale=-0.0883), {}),
+    ("BSA_ERR_SOFTMAX_SCALE", dict(softmax_scale=-1e-30), {}),
     ("BSA_ERR_TOO_LARGE", dict(mask_tiles_kv=4097), {}),
     ("BSA_ERR_NULL_POINTER", {}, dict(q=None)),
     ("BSA_ERR_NULL_POINTER", {}, dict(out=None)),
@@ -254,27 +256,28 @@ def test_sparse_decode_static_validation(lib):
 
     def dd(**kw):
         d = dict(batch=2, s_q=2, num_heads_q=128, topk=64, num_pages=10, page_size=64,
-                 max_pages_per_seq=4, softmax_scale=0.0417)
+                 softmax_scale=0.0417)
         d.update(kw)
         return DecodeDims(**d)
 
     def call_dec(dims, q=FAKE, out=FAKE, dims_ptr=True):
-        return lib.bsa_fp8_sparse_decode(q, FAKE, FAKE, FAKE, FAKE,
-                                         ctypes.byref(dims) if dims_ptr else None, out, FAKE, None)
+        return lib.bsa_fp8_sparse_decode(q, FAKE, FAKE, ctypes.byref(dims) if dims_ptr else None, out,
+                                         FAKE, None)
 
     assert call_dec(dd(), dims_ptr=False) == st["BSA_ERR_NULL_POINTER"]
     assert call_dec(dd(num_heads_q=96)) == st["BSA_ERR_GQA"]
     assert call_dec(dd(num_heads_q=0)) == st["BSA_ERR_SIZE"]
     assert call_dec(dd(topk=0)) == st["BSA_ERR_SIZE"]
     assert call_dec(dd(batch=-1)) == st["BSA_ERR_SIZE"]
-    assert call_dec(dd(page_size=16)) == st["BSA_ERR_PAGE_SIZE"]
+    assert call_dec(dd(page_size=0)) == st["BSA_ERR_PAGE_SIZE"]
+    assert call_dec(dd(page_size=-64)) == st["BSA_ERR_PAGE_SIZE"]
     assert call_dec(dd(softmax_scale=float("nan"))) == st["BSA_ERR_SOFTMAX_SCALE"]
     assert call_dec(dd(num_pages=2 ** 30, page_size=64)) == st["BSA_ERR_TOO_LARGE"]
     assert call_dec(dd(), q=None) == st["BSA_ERR_NULL_POINTER"]
     assert call_dec(dd(), out=None) == st["BSA_ERR_NULL_POINTER"]
     z = ctypes.c_void_p(0)
-    assert lib.bsa_fp8_sparse_decode(z, z, z, z, z, ctypes.byref(dd(batch=0)), z, z, None) == st["BSA_OK"]
-    assert lib.bsa_fp8_sparse_decode(z, z, z, z, z, ctypes.byref(dd(s_q=0)), z, z, None) == st["BSA_OK"]
+    assert lib.bsa_fp8_sparse_decode(z, z, z, ctypes.byref(dd(batch=0)), z, z, None) == st["BSA_OK"]
+    assert lib.bsa_fp8_sparse_decode(z, z, z, ctypes.byref(dd(s_q=0)), z, z, None) == st["BSA_OK"]
 
 
 def test_split_decode_static_validation(lib):
@@ -283,13 +286,13 @@ def test_split_decode_static_validation(lib):
 
     def dd(**kw):
         d = dict(batch=2, s_q=2, num_heads_q=128, topk=64, num_pages=10, page_size=64,
-                 max_pages_per_seq=4, softmax_scale=0.0417)
+                 softmax_scale=0.0417)
         d.update(kw)
         return DecodeDims(**d)
 
     def call_ex(dims, splits, ws=FAKE):
-        return lib.bsa_fp8_sparse_decode_ex(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(dims), splits, ws,
-                                            FAKE, FAKE, None)
+        return lib.bsa_fp8_sparse_decode_ex(FAKE, FAKE, FAKE, ctypes.byref(dims), splits, ws, FAKE, FAKE,
+                                            None)
 
     assert call_ex(dd(), 0) == st["BSA_ERR_SIZE"]
     assert call_ex(dd(), 257) == st["BSA_ERR_SIZE"]
@@ -297,14 +300,14 @@ def test_split_decode_static_validation(lib):
     assert call_ex(dd(), 2, ws=ctypes.c_void_p(0x1008)) == st["BSA_ERR_SIZE"]   # not 16-byte aligned
     # one workgroup holds at most 8192 entries: a list of 16384 needs two parts
     assert call_ex(dd(topk=16384), 1) == st["BSA_ERR_TOO_LARGE"]
-    assert lib.bsa_fp8_sparse_decode(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(dd(topk=16384)), FAKE, FAKE,
+    assert lib.bsa_fp8_sparse_decode(FAKE, FAKE, FAKE, ctypes.byref(dd(topk=16384)), FAKE, FAKE,
                                      None) == st["BSA_ERR_TOO_LARGE"]
     # 8193 entries are 257 blocks: two parts of 129 blocks (4128 entries) fit
     assert call_ex(dd(topk=8193, batch=0), 2) == st["BSA_OK"]
     assert call_ex(dd(topk=8193), 1) == st["BSA_ERR_TOO_LARGE"]
     assert call_ex(dd(topk=2 ** 21 + 1), 256) == st["BSA_ERR_TOO_LARGE"]
     z = ctypes.c_void_p(0)
-    assert lib.bsa_fp8_sparse_decode_ex(z, z, z, z, z, ctypes.byref(dd(batch=0)), 4, z, z, z, None) == st["BSA_OK"]
+    assert lib.bsa_fp8_sparse_decode_ex(z, z, z, ctypes.byref(dd(batch=0)), 4, z, z, z, None) == st["BSA_OK"]
 
 
 def test_split_decode_sizes(lib):
@@ -312,7 +315,7 @@ def test_split_decode_sizes(lib):
 
     def dd(**kw):
         d = dict(batch=2, s_q=2, num_heads_q=128, topk=2048, num_pages=10, page_size=64,
-                 max_pages_per_seq=4, softmax_scale=0.0417)
+                 softmax_scale=0.0417)
         d.update(kw)
         return DecodeDims(**d)
 

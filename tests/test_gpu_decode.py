@@ -32,12 +32,10 @@ def run_gpu(p, num_splits=None, workspace=None):
     import block_sparse_fp8_amd as bsa
     d = p.to_device("cuda")
     if num_splits is None:
-        o, l = bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"],
-                                         d["seqlens_kv"], softmax_scale=p.softmax_scale)
+        o, l = bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], softmax_scale=p.softmax_scale)
     else:
-        o, l = bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], d["block_table"],
-                                            d["seqlens_kv"], num_splits=num_splits, workspace=workspace,
-                                            softmax_scale=p.softmax_scale)
+        o, l = bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], num_splits=num_splits,
+                                            workspace=workspace, softmax_scale=p.softmax_scale)
     torch.cuda.synchronize()
     return o.float().double().cpu().numpy(), l.double().cpu().numpy()
 
@@ -108,16 +106,39 @@ def test_descales_not_powers_of_two(frac):
     compare(go2, gl2, eo, el, ea)
 
 
+def n_rows(p):
+    return p.kv_cache.shape[0] * p.kv_cache.shape[1]
+
+
 def test_empty_lists_and_sequences():
     p = make_decode_problem("decode_tiny", seed=510, lkv=(300, 0, 90), s_q=2, h_q=64, topk=40)
     p.indices[0, 1, :] = -1                          # nothing selected
-    p.indices[2, 0, :] = 90 + np.arange(40)          # everything past the sequence
+    p.indices[2, 0, :20] = n_rows(p) + np.arange(20)   # entries that name no row
+    p.indices[2, 0, 20:] = -7 - np.arange(20)
     say("[gpu] decode empty lists / empty sequence")
     go, gl = run_gpu(p)
     eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
     compare(go, gl, eo, el, ea)
     for b, s in ((0, 1), (1, 0), (1, 1), (2, 0)):
         assert np.all(go[b, s] == 0.0) and np.all(gl[b, :, s] == NEG_FLT_MAX)
+
+
+def test_rows_of_any_page():
+    """Entries are cache rows, not positions of the query's own sequence: each
+    list takes rows of every sequence's pages, in the page-block index *
+    page_size + slot encoding, with rows of physical page 0 and the last row
+    of the cache among them."""
+    p = make_decode_problem("decode_tiny", seed=514, lkv=(200, 333), s_q=2, h_q=64, topk=96)
+    rows = np.array(sorted({p.row_of(b, j) for b in range(2) for j in range(p.cfg.lkv[b])}))
+    rng = np.random.default_rng(14)
+    for b in range(2):
+        for s in range(2):
+            p.indices[b, s] = rng.choice(rows, size=96, replace=False)
+    p.indices[0, 0, :3] = [rows.min(), rows.max(), -1]
+    say("[gpu] decode rows of any page")
+    go, gl = run_gpu(p)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
 
 
 def test_repeated_entries_count_twice():
@@ -154,8 +175,7 @@ def sampled_oracle(p, go, gl, pairs):
     el = np.zeros_like(gl)
     for b, s in pairs:
         one = D.sparse_decode(p.q[b:b + 1, s:s + 1], p.kv_cache, p.indices[b:b + 1, s:s + 1],
-                              p.block_table[b:b + 1], p.seqlens_kv[b:b + 1], p.softmax_scale,
-                              with_abs=True)
+                              p.softmax_scale, with_abs=True)
         eo[b, s] = one[0][0, 0]
         el[b, :, s] = one[1][0, :, 0]
         ea[b, s] = one[2][0, 0]
@@ -200,7 +220,7 @@ def test_split_one_equals_plain_bitwise():
 def test_split_empty_lists_and_sequences():
     p = make_decode_problem("decode_tiny", seed=521, lkv=(300, 0, 90), s_q=2, h_q=64, topk=100)
     p.indices[0, 1, :] = -1
-    p.indices[2, 0, :] = 90 + np.arange(100)
+    p.indices[2, 0, :] = n_rows(p) + np.arange(100)   # entries that name no row
     p.indices[0, 0, 32:] = -1                      # only the first part selects anything
     say("[gpu] split decode empty lists / empty sequence")
     go, gl = run_gpu(p, num_splits=4)

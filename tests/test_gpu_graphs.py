@@ -56,12 +56,11 @@ def test_decode_graph_replays(split):
 
     def call(o, l):
         if split:
-            bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], d["block_table"], d["seqlens_kv"],
-                                         num_splits=splits, workspace=ws, softmax_scale=p.softmax_scale,
-                                         out=o, lse=l)
+            bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], num_splits=splits, workspace=ws,
+                                         softmax_scale=p.softmax_scale, out=o, lse=l)
         else:
-            bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], d["block_table"], d["seqlens_kv"],
-                                      softmax_scale=p.softmax_scale, out=o, lse=l)
+            bsa.bsa_fp8_sparse_decode(d["q"], d["kv_cache"], d["indices"], softmax_scale=p.softmax_scale,
+                                      out=o, lse=l)
 
     say(f"[gpu] graph decode split={split}")
     g = capture(lambda: call(out, lse))

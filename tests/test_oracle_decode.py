@@ -1,6 +1,8 @@
 """Pins of the FP8 sparse decode oracle (oracle/decode.py): a hand-built cache
-row, a scalar brute force, closed forms, the handling of invalid and repeated
-indices, invariances, and dense attention against torch."""
+row, hand-built index entries (page-block index * page_block_size + offset,
+-1 unused: the FlashMLA FP8 sparse decoding article, quick-reproduce
+paragraph), a scalar brute force, closed forms, the handling of invalid and
+repeated indices, invariances, and dense attention against torch."""
 import math
 import struct
 
@@ -30,6 +32,43 @@ def test_hand_built_row():
     assert np.count_nonzero(k) == 7
 
 
+def _marked_cache(num_pages, page_size):
+    """A cache whose row (page g, slot t) has code 1.0 at dimension 0, zeros
+    elsewhere and descale 1 + g * page_size + t on its first tile, so a decode
+    over one entry returns that number at output dimension 0."""
+    cache = np.zeros((num_pages, page_size, 656), dtype=np.uint8)
+    for g in range(num_pages):
+        for t in range(page_size):
+            cache[g, t, 0] = 0x38                                   # E4M3 1.0
+            cache[g, t, 512:528] = np.frombuffer(
+                struct.pack("<4f", 1.0 + g * page_size + t, 1.0, 1.0, 1.0), dtype=np.uint8)
+    return cache
+
+
+def test_hand_built_index_entries():
+    """Entry e names the row at page e // page_size, slot e % page_size: the
+    row of physical page 2, slot 5 of a 32-slot cache is entry 2 * 32 + 5 = 69."""
+    cache = _marked_cache(num_pages=3, page_size=32)
+    q = np.zeros((1, 5, 2, 576))
+    idx = np.full((1, 5, 4), -1, dtype=np.int32)
+    idx[0, 0, 2] = 69                     # page 2, slot 5
+    idx[0, 1, 0] = 0                      # page 0, slot 0
+    idx[0, 2, 3] = 95                     # the last row: page 2, slot 31
+    idx[0, 3, :] = [96, -2, 1000, -1]     # past the cache, negative: no row
+    idx[0, 4, :2] = [37, 37]              # page 1, slot 5, listed twice
+    o, lse = D.sparse_decode(q, cache, idx, softmax_scale=0.1)
+    assert o[0, 0, 0, 0] == 1.0 + 2 * 32 + 5 and np.count_nonzero(o[0, 0]) == 2
+    assert o[0, 1, 0, 0] == 1.0
+    assert o[0, 2, 0, 0] == 1.0 + 2 * 32 + 31
+    assert np.all(o[0, 3] == 0) and np.all(lse[0, :, 3] == D.NEG_FLT_MAX)
+    assert o[0, 4, 0, 0] == 1.0 + 32 + 5 and lse[0, 0, 4] == math.log(2.0)
+    assert np.all(lse[0, :, :3] == 0.0)   # one entry, zero query: ln 1
+    # the same entry read with the page size as 64 names another row
+    cache64 = _marked_cache(num_pages=2, page_size=64)
+    o64, _ = D.sparse_decode(q[:, :1], cache64, idx[:, :1], softmax_scale=0.1)
+    assert o64[0, 0, 0, 0] == 1.0 + 69
+
+
 def scalar_dequant(row):
     scales = struct.unpack("<4f", bytes(row[512:528]))
     out = []
@@ -50,9 +89,9 @@ def test_brute_force_tiny():
             for h in range(3):
                 terms = []
                 for j in p.indices[b, s]:
-                    if not 0 <= j < p.seqlens_kv[b]:
+                    if not 0 <= j < p.kv_cache.shape[0] * ps:
                         continue
-                    row = p.kv_cache[p.block_table[b, j // ps], j % ps]
+                    row = p.kv_cache[j // ps, j % ps]
                     k = scalar_dequant(row)
                     sc = p.softmax_scale * sum(float(p.q[b, s, h, d]) * k[d] for d in range(576))
                     terms.append((sc, k[:512]))
@@ -74,8 +113,8 @@ def test_zero_query_closed_form():
     for b in range(2):
         for s in range(2):
             idx = p.indices[b, s]
-            idx = idx[(idx >= 0) & (idx < p.seqlens_kv[b])]
-            k = D.dequant_rows(D.gather_rows(p.kv_cache, p.block_table, b, idx))
+            idx = idx[(idx >= 0) & (idx < p.kv_cache.shape[0] * p.kv_cache.shape[1])]
+            k = D.dequant_rows(D.gather_rows(p.kv_cache, idx))
             np.testing.assert_allclose(o[b, s], np.broadcast_to(k[:, :512].mean(axis=0), o[b, s].shape),
                                        rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(lse[b, :, s], math.log(idx.size), rtol=1e-12)
@@ -84,10 +123,10 @@ def test_zero_query_closed_form():
 def test_single_entry_and_empty():
     p = make_decode_problem("decode_tiny", seed=7)
     p.indices[:] = -1
-    p.indices[0, 0, 5] = 17
-    p.indices[1, 1, 0] = p.seqlens_kv[1] + 3      # past the sequence: not attended
+    p.indices[0, 0, 5] = p.row_of(0, 17)
+    p.indices[1, 1, 0] = p.kv_cache.shape[0] * p.kv_cache.shape[1]   # past the cache: no row
     o, lse = D.sparse_decode(**p.oracle_kwargs())
-    k = D.dequant_rows(D.gather_rows(p.kv_cache, p.block_table, 0, np.array([17])))[0]
+    k = D.dequant_rows(D.gather_rows(p.kv_cache, np.array([p.row_of(0, 17)])))[0]
     np.testing.assert_allclose(o[0, 0], np.broadcast_to(k[:512], o[0, 0].shape), rtol=1e-14)
     np.testing.assert_allclose(lse[0, :, 0], p.softmax_scale * (p.q[0, 0].astype(np.float64) @ k), rtol=1e-12)
     for b, s in ((0, 1), (1, 0), (1, 1)):
@@ -112,13 +151,13 @@ def test_repeated_entry_equals_a_copied_token():
     """Listing token j twice equals listing j and an identical copy of it."""
     p = make_decode_problem("decode_tiny", lkv=(130, 70), seed=9, ragged=False, topk=20)
     ps = p.kv_cache.shape[1]
-    j, spare = int(p.indices[0, 0, 0]), 129            # position 129 holds a copy of j
-    src = p.kv_cache[p.block_table[0, j // ps], j % ps].copy()
+    j, spare = int(p.indices[0, 0, 0]), p.row_of(0, 129)   # position 129 holds a copy of row j
+    src = p.kv_cache[j // ps, j % ps].copy()
     p.indices[0, 0] = np.where(p.indices[0, 0] == spare, -1, p.indices[0, 0])
     q = make_decode_problem("decode_tiny", lkv=(130, 70), seed=9, ragged=False, topk=20)
     q.indices = p.indices.copy()
     p.indices[0, 0, -1] = j
-    q.kv_cache[q.block_table[0, spare // ps], spare % ps] = src
+    q.kv_cache[spare // ps, spare % ps] = src
     q.indices[0, 0, -1] = spare
     o1, l1 = D.sparse_decode(**p.oracle_kwargs())
     o2, l2 = D.sparse_decode(**q.oracle_kwargs())
@@ -140,11 +179,12 @@ def test_dense_selection_matches_torch_attention():
     p = make_decode_problem("decode_tiny", lkv=(150, 90), s_q=1, h_q=4, topk=150, seed=11)
     for b in range(2):                                  # every token, in order
         p.indices[b, 0] = -1
-        p.indices[b, 0, :p.seqlens_kv[b]] = np.arange(p.seqlens_kv[b])
+        p.indices[b, 0, :p.seqlens_kv[b]] = [p.row_of(b, j) for j in range(p.seqlens_kv[b])]
     o, lse = D.sparse_decode(**p.oracle_kwargs())
     for b in range(2):
         n = int(p.seqlens_kv[b])
-        k = torch.from_numpy(D.dequant_rows(D.gather_rows(p.kv_cache, p.block_table, b, np.arange(n))))
+        rows = np.array([p.row_of(b, j) for j in range(n)])
+        k = torch.from_numpy(D.dequant_rows(D.gather_rows(p.kv_cache, rows)))
         q = torch.from_numpy(p.q[b, 0].astype(np.float64))                     # [h, 576]
         ref = torch.nn.functional.scaled_dot_product_attention(
             q[:, None, :], k[None].expand(4, n, 576), k[None, :, :512].expand(4, n, 512),
@@ -162,7 +202,8 @@ def test_abs_weighted_output():
     ps = p.kv_cache.shape[1]
     for b in range(2):                 # make every value positive: A equals O
         for j in range(p.seqlens_kv[b]):
-            row = p.kv_cache[p.block_table[b, j // ps], j % ps]
+            r = p.row_of(b, j)
+            row = p.kv_cache[r // ps, r % ps]
             row[:512] &= 0x7F            # clear the sign of every code (descales are positive)
     o, lse, a = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
     np.testing.assert_allclose(a, o, rtol=1e-12, atol=0)
