@@ -253,6 +253,10 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
     {
       const uint8_t* sb = stage_lds + (n % kStages) * (NW * kWaveStage) + wave * kWaveStage;
       uint8_t* dst = k_lds + ltok * kKStride;
+      // An entry that names no row was staged from row 0, which may hold
+      // anything: its K/V values are written as zeros, so that its zero
+      // probability cannot meet a NaN or infinity in the P.V product.
+      const bool tok_valid = rows_lds[n * kBlock + ltok] >= 0;
       // lane of part 0 of this token within the wave (16-lane layout: its round 2
       // holds the four descales)
 #pragma unroll
@@ -261,7 +265,8 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         const uint8_t* rb = sb + 3 * h * kRound;                 // this lane's rounds for pp
         // the four descales: round 2 of the token's first lane (part 0)
         const int lane0 = ln & ~(kTokThreads - 1);
-        const float scale = *reinterpret_cast<const float*>(sb + 2 * kRound + 16 * lane0 + 4 * (pp >> 2));
+        const float scale =
+            tok_valid ? *reinterpret_cast<const float*>(sb + 2 * kRound + 16 * lane0 + 4 * (pp >> 2)) : 1.0f;
         // A power-of-two descale in [2^-100, 2^100] (the format's own: amax/448
         // rounded up to a power of two) makes code * descale exact in bfloat16,
         // and v_cvt_scalef32_pk_bf16_fp8, which applies only the scale's
@@ -272,7 +277,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         const bool pow2 = (su & 0x807fffffu) == 0 && (su >> 23) >= 27 && (su >> 23) <= 227;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const v4i codes = *reinterpret_cast<const v4i*>(rb + i * kRound + 16 * ln);
+          const v4i codes = tok_valid ? *reinterpret_cast<const v4i*>(rb + i * kRound + 16 * ln) : v4i{0, 0, 0, 0};
           uint32_t w[8];
           if (pow2) {
 #pragma unroll
@@ -297,7 +302,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         }
         if (pp >= 1 && pp <= 8)
           *reinterpret_cast<v4i*>(dst + 2 * (kDimV + 8 * (pp - 1))) =
-              *reinterpret_cast<const v4i*>(rb + 2 * kRound + 16 * ln);
+              tok_valid ? *reinterpret_cast<const v4i*>(rb + 2 * kRound + 16 * ln) : v4i{0, 0, 0, 0};
       }
     }
     // block n+2 into the buffer block n-1 used (this wave's reads of it are done)

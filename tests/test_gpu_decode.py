@@ -141,6 +141,23 @@ def test_rows_of_any_page():
     say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
 
 
+def test_unused_entries_with_nan_in_row_zero():
+    """Entries that name no row are staged from row 0; with NaN codes,
+    descales and RoPE values there, the result must still be finite and equal
+    the oracle's, which never reads an unnamed row."""
+    p = make_decode_problem("decode_tiny", seed=515, lkv=(300, 1000), s_q=2, h_q=64, topk=200, ragged=True)
+    ps = p.kv_cache.shape[1]
+    p.indices[(p.indices >= 0) & (p.indices < ps)] = -1    # nothing names page 0
+    p.kv_cache[0, :, :512] = 0x7F                          # E4M3 NaN
+    p.kv_cache[0, :, 512:] = 0xFF                          # NaN descales and bfloat16 NaN
+    assert (p.indices == -1).any()
+    say("[gpu] decode unused entries, NaN in row 0")
+    for splits in (None, 3):
+        go, gl = run_gpu(p, num_splits=splits)
+        eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+        say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
+
+
 def test_repeated_entries_count_twice():
     p = make_decode_problem("decode_tiny", seed=511, lkv=(400,), s_q=1, h_q=64, topk=50)
     p.indices[0, 0, 25:] = p.indices[0, 0, :25]       # every token listed twice
