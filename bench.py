@@ -422,6 +422,8 @@ def main():
     ap.add_argument("--splits", default="auto",
                     help="decode only: parts per index list (an integer, or 'auto' for the library's "
                          "choice; 1 is the single-pass kernel)")
+    ap.add_argument("--qk", choices=("default", "f16", "fp8"), default="default",
+                    help="matrix path of the prefill's Q.K^T products (bsa_qk_precision)")
     ap.add_argument("--schedule", action="store_true",
                     help="run the scheduling pre-pass inside every step and launch the prefill "
                          "in its task order")
@@ -487,8 +489,10 @@ def main():
                              max_seqlen_q=p.max_seqlen_q, causal=p.causal, sparse_indices=si,
                              sparse_seq_len=sl, workspace=ws, schedule=sched)
 
+    qk = {"default": 0, "f16": 1, "fp8": 2}[args.qk]
+
     def step():
-        if args.form == "mask" and not args.schedule:
+        if args.form == "mask" and not args.schedule and qk == 0:
             bsa.bsa_fp8_prefill(d["q"], d["kcache"], d["vcache"], d["qscale"], d["kscale"],
                                 d["vscale"], d["cu_seqlens_q"], d["block_table"], d["seqlens_kv"],
                                 d["block_mask"], p.quant_type, p.page_size,
@@ -502,7 +506,7 @@ def main():
                                mask, p.quant_type, p.page_size, max_seqlen_q=p.max_seqlen_q,
                                kv_layout=p.kv_layout, causal=p.causal,
                                softmax_scale=p.softmax_scale, sparse_indices=si,
-                               sparse_seq_len=sl, schedule=sched, out=out, lse=lse)
+                               sparse_seq_len=sl, schedule=sched, qk_precision=qk, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -568,7 +572,7 @@ def main():
         "data": "synthetic (seeded N(0,1) quantised to E4M3, random paging and block mask)",
         "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "active_tiles": n_act,
                    "q_tokens": T, "causal": bool(p.causal), "sparsity_form": args.form,
-                   "schedule_pre_pass": bool(args.schedule)},
+                   "schedule_pre_pass": bool(args.schedule), "qk_precision": args.qk},
         "tokens_per_s": round(T / (wall / args.steps), 1),
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "useful_tflops": round(pairs * 4 * TILE / (wall / args.steps) / 1e12, 2),

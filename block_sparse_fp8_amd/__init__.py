@@ -19,6 +19,7 @@ __all__ = [
     "KVLayout",
     "BsaError",
     "QLayout",
+    "QKPrecision",
     "bsa_fp8_prefill",
     "bsa_fp8_prefill_ex",
     "bsa_fp8_schedule",
@@ -58,6 +59,13 @@ class QLayout(enum.IntEnum):
     """Query layouts ("Quant Block Sparse Attention", "Key parameters")."""
     TND = 0  # q [T, Hq, 128], qscale [T, Hq]
     NTD = 1  # q [Hq, T, 128], qscale [Hq, T]
+
+
+class QKPrecision(enum.IntEnum):
+    """Matrix path of the prefill's Q.K^T products (bsa_qk_precision)."""
+    DEFAULT = 0  # the library's choice
+    F16 = 1      # E4M3 widened exactly to f16, f16 matrix products
+    FP8 = 2      # E4M3 operands on the FP8 matrix products
 
 
 class ScaleMode(enum.IntEnum):
@@ -101,6 +109,7 @@ class Options(ctypes.Structure):
         ("sparse_seq_len", ctypes.c_void_p),
         ("schedule", ctypes.c_void_p),
         ("schedule_len", ctypes.c_int32),
+        ("qk_precision", ctypes.c_int32),
     ]
 
 
@@ -201,18 +210,19 @@ def _sparsity_shape(block_mask, sparse_indices, sparse_seq_len, device):
     return 0, 0
 
 
-def _options(q_layout, p_scale, sparse_indices, sparse_seq_len, schedule):
+def _options(q_layout, p_scale, sparse_indices, sparse_seq_len, schedule, qk_precision=0):
     return Options(q_layout=int(q_layout), p_scale=0.0 if p_scale is None else float(p_scale),
                    sparse_indices=None if sparse_indices is None else sparse_indices.data_ptr(),
                    sparse_seq_len=None if sparse_seq_len is None else sparse_seq_len.data_ptr(),
                    schedule=None if schedule is None else schedule.data_ptr(),
-                   schedule_len=0 if schedule is None else schedule.numel())
+                   schedule_len=0 if schedule is None else schedule.numel(),
+                   qk_precision=int(qk_precision))
 
 
 def _prefill(entry, q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, block_table,
              seqlens_kv, block_mask, quant_type, page_size, max_seqlen_q, kv_layout, causal,
              softmax_scale, out, lse, return_lse, stream, q_layout=QLayout.TND, p_scale=None,
-             sparse_indices=None, sparse_seq_len=None, schedule=None):
+             sparse_indices=None, sparse_seq_len=None, schedule=None, qk_precision=0):
     device = q.device
     if device.type != "cuda":
         raise ValueError(entry + " runs on a GPU; q is on " + str(device))
@@ -260,7 +270,7 @@ def _prefill(entry, q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, blo
             _ptr(cu_seqlens_q), _ptr(block_table), _ptr(seqlens_kv), _ptr(mask_u8),
             int(quant_type), int(page_size), ctypes.byref(dims)]
     if entry == "bsa_fp8_prefill_ex":
-        opts = _options(q_layout, p_scale, sparse_indices, sparse_seq_len, schedule)
+        opts = _options(q_layout, p_scale, sparse_indices, sparse_seq_len, schedule, qk_precision)
         args.append(ctypes.byref(opts))
     args += [_ptr(out), _ptr(lse), ctypes.c_void_p(stream)]
     status = getattr(lib, entry)(*args)
@@ -287,18 +297,19 @@ def bsa_fp8_prefill_ex(q, kcache, vcache, qscale, kscale, vscale, cu_seqlens_q, 
                        seqlens_kv, block_mask, quant_type, page_size, *, max_seqlen_q,
                        kv_layout=KVLayout.NHD, causal=True, softmax_scale=None,
                        q_layout=QLayout.TND, p_scale=None, sparse_indices=None,
-                       sparse_seq_len=None, schedule=None,
+                       sparse_seq_len=None, schedule=None, qk_precision=QKPrecision.DEFAULT,
                        out=None, lse=None, return_lse=True, stream=None):
     """Call the C entry point of the same name: bsa_fp8_prefill plus the query
     layout (q [Hq,T,128] and qscale [Hq,T] for NTD), the P-scale (None = 256),
     the index-list sparsity (sparse_indices int32 [B,Hq,Qb,Kb] with
-    sparse_seq_len int32 [B,Hq,Qb], instead of block_mask) and a task order
-    from ``bsa_fp8_schedule``.  Returns (out, lse); out is TND."""
+    sparse_seq_len int32 [B,Hq,Qb], instead of block_mask), a task order
+    from ``bsa_fp8_schedule`` and the matrix path of Q.K^T (QKPrecision).
+    Returns (out, lse); out is TND."""
     return _prefill("bsa_fp8_prefill_ex", q, kcache, vcache, qscale, kscale, vscale,
                     cu_seqlens_q, block_table, seqlens_kv, block_mask, quant_type, page_size,
                     max_seqlen_q, kv_layout, causal, softmax_scale, out, lse, return_lse, stream,
                     q_layout=q_layout, p_scale=p_scale, sparse_indices=sparse_indices,
-                    sparse_seq_len=sparse_seq_len, schedule=schedule)
+                    sparse_seq_len=sparse_seq_len, schedule=schedule, qk_precision=qk_precision)
 
 
 def _schedule_dims(batch, num_heads_q, max_seqlen_q, mt, mkv, causal):

@@ -201,7 +201,7 @@ struct ListWalk {
   }
 };
 
-template <int QUANT, int FORM>
+template <int QUANT, int FORM, bool QK8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bsa_fp8_prefill_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t k16_lds[kTile * kK16Row];       // 32 KB
@@ -289,8 +289,20 @@ bsa_fp8_prefill_kernel(Params p) {
   // Q operand (B of S^T = K.Q^T, f16 32x32x16): lane holds query `col`,
   // head-dim elements ks*16 + hd*8 .. +7 for ks = 0..7.
   v8h qh[8];
+  v8i q8[2];  // FP8 products: lane holds query `col`, dims ks*64 + hd*32 .. +31
   float cscale = 0.0f;
-  {
+  if constexpr (QK8) {
+    if (q_valid) {
+      const int64_t qi = (int64_t)(t0 + tq) * p.q_tok_stride + (int64_t)h * p.q_head_stride;
+      const uint8_t* qp = p.q + qi * kHeadDim + hd * 32;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) q8[ks] = *reinterpret_cast<const v8i*>(qp + ks * 64);
+      cscale = p.qscale[qi] * p.qk_scale;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) q8[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  } else {
     v2i raw[8];
     if (q_valid) {
       const int64_t qi = (int64_t)(t0 + tq) * p.q_tok_stride + (int64_t)h * p.q_head_stride;
@@ -440,15 +452,22 @@ bsa_fp8_prefill_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) kreg[i] = v4i{0, 0, 0, 0};
     }
+    if constexpr (QK8) {
+      // E4M3 kept as is, chunk-major: 16-byte chunk c (dims 16c..16c+15) of
+      // key row r at c*2048 + r*16.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const v2i a = e4m3x4_to_f16x4((uint32_t)kreg[i][0]);
-      const v2i c = e4m3x4_to_f16x4((uint32_t)kreg[i][1]);
-      const v2i d = e4m3x4_to_f16x4((uint32_t)kreg[i][2]);
-      const v2i e = e4m3x4_to_f16x4((uint32_t)kreg[i][3]);
-      const int chunk = 8 * khalf + 2 * i;
-      *reinterpret_cast<v4i*>(k16_lds + chunk * 2048 + krow * 16) = v4i{a[0], a[1], c[0], c[1]};
-      *reinterpret_cast<v4i*>(k16_lds + (chunk + 1) * 2048 + krow * 16) = v4i{d[0], d[1], e[0], e[1]};
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i*>(k16_lds + (4 * khalf + i) * 2048 + krow * 16) = kreg[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v2i a = e4m3x4_to_f16x4((uint32_t)kreg[i][0]);
+        const v2i c = e4m3x4_to_f16x4((uint32_t)kreg[i][1]);
+        const v2i d = e4m3x4_to_f16x4((uint32_t)kreg[i][2]);
+        const v2i e = e4m3x4_to_f16x4((uint32_t)kreg[i][3]);
+        const int chunk = 8 * khalf + 2 * i;
+        *reinterpret_cast<v4i*>(k16_lds + chunk * 2048 + krow * 16) = v4i{a[0], a[1], c[0], c[1]};
+        *reinterpret_cast<v4i*>(k16_lds + (chunk + 1) * 2048 + krow * 16) = v4i{d[0], d[1], e[0], e[1]};
+      }
     }
     __syncthreads();  // k16 ready
     if (n1 >= 0) issue_k(n1, pg[buf ^ 1], ln);
@@ -464,7 +483,25 @@ bsa_fp8_prefill_kernel(Params p) {
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[c][r] = 0.0f;
-    {
+    if constexpr (QK8) {
+      // FP8 products (v_mfma_f32_32x32x64_f8f6f4): two k-steps of 64 dims;
+      // lane half h reads dims ks*64 + 32h .. +31 of its key row (chunks
+      // 4ks + 2h and 4ks + 2h + 1).
+      const int hi_a = (lcol >> 2) & 1;
+      const int ri_a = ((lcol >> 3) << 2) | (lcol & 3);
+      const uint8_t* kp = k16_lds + 2 * lhd * 2048 + (hi_a * 32 + ri_a) * 16;
+      auto kread = [&](int c, int ks) -> v8i {
+        const uint8_t* a = kp + ((c >> 1) * 64 + (c & 1) * 16) * 16 + ks * 4 * 2048;
+        const v4i lo = *reinterpret_cast<const v4i*>(a);
+        const v4i hi = *reinterpret_cast<const v4i*>(a + 2048);
+        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      v8i ka[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) ka[x] = kread(x & 3, x >> 2);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) s[x & 3] = mfma_f8(ka[x], q8[x >> 2], s[x & 3]);
+    } else {
       const int hi_a = (lcol >> 2) & 1;
       const int ri_a = ((lcol >> 3) << 2) | (lcol & 3);
       const uint8_t* kp = k16_lds + lhd * 2048 + (hi_a * 32 + ri_a) * 16;
@@ -705,16 +742,15 @@ int bsa_fp8_prefill_ex(const void* q, const void* kcache, const void* vcache, co
   const dim3 grid3((unsigned)grid), block3(kThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool list = r.form == bsa::kFormList;
-  if (quant_type == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR) {
-    if (list)
-      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR, kFormList>), grid3, block3, 0, s, p);
-    else
-      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR, 0>), grid3, block3, 0, s, p);
+  const bool q1 = quant_type == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD;
+  constexpr int Q0 = BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR, Q1 = BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid3, block3, 0, s, p); };
+  if (r.qk8) {
+    if (q1) list ? go(bsa_fp8_prefill_kernel<Q1, kFormList, true>) : go(bsa_fp8_prefill_kernel<Q1, 0, true>);
+    else list ? go(bsa_fp8_prefill_kernel<Q0, kFormList, true>) : go(bsa_fp8_prefill_kernel<Q0, 0, true>);
   } else {
-    if (list)
-      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD, kFormList>), grid3, block3, 0, s, p);
-    else
-      hipLaunchKernelGGL((bsa_fp8_prefill_kernel<BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD, 0>), grid3, block3, 0, s, p);
+    if (q1) list ? go(bsa_fp8_prefill_kernel<Q1, kFormList, false>) : go(bsa_fp8_prefill_kernel<Q1, 0, false>);
+    else list ? go(bsa_fp8_prefill_kernel<Q0, kFormList, false>) : go(bsa_fp8_prefill_kernel<Q0, 0, false>);
   }
   if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
   return BSA_OK;

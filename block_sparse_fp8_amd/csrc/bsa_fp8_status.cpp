@@ -26,6 +26,7 @@ const char* bsa_fp8_status_string(int status) {
     case BSA_ERR_SPARSE_FORM: return "give block_mask or sparse_indices with sparse_seq_len, not both";
     case BSA_ERR_SCHEDULE: return "schedule_len must equal the task count";
     case BSA_ERR_SCALE_MODE: return "unknown scale_mode";
+    case BSA_ERR_QK_PRECISION: return "unknown qk_precision";
     default: return "unknown status";
   }
 }

@@ -45,6 +45,7 @@ struct Resolved {
   int q_layout;
   float p_scale;
   const int32_t* schedule;
+  bool qk8;          // Q.K^T on the FP8 matrix path
 };
 
 inline bool finite_float(float x) {
@@ -94,6 +95,8 @@ inline int resolve(const bsa_fp8_dims* dims, const uint8_t* block_mask, const bs
   const int64_t tasks = (int64_t)d.batch * d.num_heads_q * mt_grid;
   if (tasks > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
   if (o.schedule != nullptr && o.schedule_len != tasks) return BSA_ERR_SCHEDULE;
+  if (o.qk_precision != BSA_QK_DEFAULT && o.qk_precision != BSA_QK_F16 && o.qk_precision != BSA_QK_FP8)
+    return BSA_ERR_QK_PRECISION;
 
   r->d = d;
   r->group = group;
@@ -105,6 +108,7 @@ inline int resolve(const bsa_fp8_dims* dims, const uint8_t* block_mask, const bs
   r->q_layout = o.q_layout;
   r->p_scale = ps;
   r->schedule = o.schedule;
+  r->qk8 = o.qk_precision == BSA_QK_FP8;
   return BSA_OK;
 }
 

@@ -90,7 +90,8 @@ typedef enum {
     BSA_ERR_SPARSE_FORM = 14,  /* block_mask and sparse_indices both given, or
                                   only one of sparse_indices / sparse_seq_len   */
     BSA_ERR_SCHEDULE = 15,     /* schedule_len does not match the task count    */
-    BSA_ERR_SCALE_MODE = 16    /* scale_mode not a bsa_scale_mode               */
+    BSA_ERR_SCALE_MODE = 16,   /* scale_mode not a bsa_scale_mode               */
+    BSA_ERR_QK_PRECISION = 17  /* options->qk_precision not a bsa_qk_precision  */
 } bsa_status;
 
 /* How bsa_fp8_quantize_append computes a descale from a row's largest
@@ -105,6 +106,18 @@ typedef enum {
     BSA_Q_TND = 0, /* q E4M3 [T, Hq, 128], qscale float [T, Hq] */
     BSA_Q_NTD = 1  /* q E4M3 [Hq, T, 128], qscale float [Hq, T] */
 } bsa_q_layout;
+
+/* Matrix path of the Q.K^T products of the prefill.  The hpc-ops article
+ * ("FP8 Tensor Core compute") runs both products on FP8 matrix units.  On
+ * gfx950 the FP8 products keep fewer bits below the largest term of each
+ * dot product than an fp32 sum does; the f16 path widens the E4M3 operands
+ * exactly and sums with fp32-like accuracy.  Both feed the same softmax, P
+ * quantisation and FP8 P.V product. */
+typedef enum {
+    BSA_QK_DEFAULT = 0, /* the library's choice (BSA_QK_F16)                  */
+    BSA_QK_F16 = 1,     /* E4M3 widened exactly to f16, f16 matrix products  */
+    BSA_QK_FP8 = 2      /* E4M3 operands on the FP8 matrix products          */
+} bsa_qk_precision;
 
 /* Largest block-mask width (KV tiles of 128 keys) a masked call accepts:
  * 4096 tiles = 524288 keys.  A call with block_mask == NULL has no limit. */
@@ -191,6 +204,7 @@ int bsa_fp8_prefill(const void* q, const void* kcache, const void* vcache,
  *                 ceil(Lkv_b/128), or wholly above the causal range of the Q
  *                 tile select no keys and are skipped.  A tile id must not
  *                 repeat within a row (caller's contract).
+ * qk_precision    bsa_qk_precision of the Q.K^T products.
  * schedule        NULL, or the task order written by bsa_fp8_schedule for the
  * schedule_len    same sparsity, sequence lengths and dims; schedule_len is
  *                 then the task count B * Hq * ceil(max_seqlen_q / 128).
@@ -204,6 +218,7 @@ typedef struct {
     const int32_t* sparse_seq_len;
     const int32_t* schedule;
     int32_t schedule_len;
+    int32_t qk_precision;
 } bsa_fp8_options;
 
 /*

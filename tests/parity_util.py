@@ -42,6 +42,21 @@ def tile_rows(problem, tiles):
     return sel
 
 
+def stats_of(got_o, got_l, emu_o, emu_l, exact_o, sel=None):
+    """The quantities the acceptance rule looks at, without asserting."""
+    if sel is None:
+        sel = np.ones(got_o.shape[:2], dtype=bool)
+    go, eo, xo = got_o[sel], emu_o[sel], exact_o[sel]
+    gl, el = got_l.T[sel], emu_l.T[sel]
+    bad_o = np.abs(go - eo) > O_ATOL + O_RTOL * np.abs(eo)
+    bad_l = np.abs(gl - el) > L_ATOL + L_RTOL * np.abs(el)
+    return dict(n=int(go.size), frac_o=float(bad_o.mean()) if bad_o.size else 0.0,
+                frac_lse=float(bad_l.mean()) if bad_l.size else 0.0,
+                max_abs_vs_emulate=float(np.abs(go - eo).max()) if go.size else 0.0,
+                max_abs_vs_exact=float(np.abs(go - xo).max()) if go.size else 0.0,
+                finite=bool(np.all(np.isfinite(go)) and np.all(np.isfinite(gl))))
+
+
 def compare(got_o, got_l, emu_o, emu_l, exact_o, sel=None, exact_bound=None):
     """Assert the acceptance rule; return a dict of statistics.
 
@@ -75,7 +90,7 @@ def compare(got_o, got_l, emu_o, emu_l, exact_o, sel=None, exact_bound=None):
 
 
 def run_gpu_ex(problem, mask=True, causal=None, q_layout=0, p_scale=None, index_form=None,
-               schedule=None):
+               schedule=None, qk_precision=0):
     """Run bsa_fp8_prefill_ex on cuda:0: optional NTD queries, P-scale, index
     lists (sparse_indices, sparse_seq_len) instead of the mask, and a task
     order.  Returns (out float64 [T,Hq,128], lse float64 [Hq,T])."""
@@ -100,7 +115,7 @@ def run_gpu_ex(problem, mask=True, causal=None, q_layout=0, p_scale=None, index_
         problem.quant_type, problem.page_size, max_seqlen_q=problem.max_seqlen_q,
         kv_layout=problem.kv_layout, causal=problem.causal if causal is None else causal,
         softmax_scale=problem.softmax_scale, q_layout=q_layout, p_scale=p_scale,
-        sparse_indices=si, sparse_seq_len=sl, schedule=sched)
+        sparse_indices=si, sparse_seq_len=sl, schedule=sched, qk_precision=qk_precision)
     torch.cuda.synchronize()
     return o.float().double().cpu().numpy(), l.double().cpu().numpy()
 
