@@ -27,6 +27,7 @@ __all__ = [
     "bsa_fp8_quantize_append",
     "bsa_fp8_sparse_decode",
     "bsa_fp8_sparse_decode_ex",
+    "bsa_fp8_sparse_decode_noalloc",
     "bsa_fp8_sparse_decode_workspace_bytes",
     "bsa_fp8_sparse_decode_num_splits",
     "DecodeDims",
@@ -158,6 +159,9 @@ def load_library():
     lib.bsa_fp8_sparse_decode_ex.argtypes = [vp, vp, vp, ctypes.POINTER(DecodeDims),
                                              ctypes.c_int, vp, vp, vp, vp]
     lib.bsa_fp8_sparse_decode_ex.restype = ctypes.c_int
+    lib.bsa_fp8_sparse_decode_noalloc.argtypes = [vp, vp, vp, ctypes.POINTER(DecodeDims), ctypes.c_int,
+                                                  vp, vp, vp]
+    lib.bsa_fp8_sparse_decode_noalloc.restype = ctypes.c_int
     lib.bsa_fp8_sparse_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeDims), ctypes.c_int]
     lib.bsa_fp8_sparse_decode_workspace_bytes.restype = ctypes.c_longlong
     lib.bsa_fp8_sparse_decode_num_splits.argtypes = [ctypes.POINTER(DecodeDims)]
@@ -534,6 +538,38 @@ def bsa_fp8_sparse_decode_ex(q, kv_cache, indices, *, num_splits="auto", workspa
     bsa_fp8_sparse_decode_workspace_bytes bytes, allocated here when None."""
     return _sparse_decode(q, kv_cache, indices, softmax_scale, out, lse, return_lse, stream, num_splits,
                           workspace)
+
+
+def bsa_fp8_sparse_decode_noalloc(q, kv_cache, indices, out, lse, *, num_splits=0, softmax_scale=None,
+                                  stream=None):
+    """Call the C entry point of the same name: the split-list decode with its
+    partial results in the library's static scratch, so nothing is allocated
+    on the device by this call.  ``out`` (bf16 [B, s_q, h_q, 512]) and ``lse``
+    (float32 [B, h_q, s_q] or None) are the caller's.  num_splits 0 = the
+    library's choice within the scratch."""
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("bsa_fp8_sparse_decode_noalloc runs on a GPU; q is on " + str(device))
+    _check("q", q, (torch.bfloat16,), device)
+    _check("kv_cache", kv_cache, (torch.uint8,), device)
+    _check("indices", indices, (torch.int32,), device)
+    _check("out", out, (torch.bfloat16,), device)
+    if lse is not None:
+        _check("lse", lse, (torch.float32,), device)
+    if q.dim() != 4 or q.shape[3] != 576 or kv_cache.shape[-1] != 656:
+        raise ValueError("q must be [B, s_q, h_q, 576] and kv_cache [num_pages, page_size, 656]")
+    B, s_q, h_q, _ = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(576)
+    dims = _decode_dims(B, s_q, h_q, indices.shape[2], kv_cache.shape[0], kv_cache.shape[1], softmax_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    status = load_library().bsa_fp8_sparse_decode_noalloc(
+        _ptr(q), _ptr(kv_cache), _ptr(indices), ctypes.byref(dims), int(num_splits), _ptr(out), _ptr(lse),
+        ctypes.c_void_p(stream))
+    if status != 0:
+        raise BsaError(status, status_string(status))
+    return out, lse
 
 
 def attention_with_kvcache_blocksparse_prefill_fp8(

@@ -51,6 +51,8 @@
 #include "bsa_fp8.h"
 #include "bsa_internal.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int kBlock = 32;          // tokens per iteration
@@ -500,6 +502,104 @@ __global__ void __launch_bounds__(128) bsa_fp8_decode_combine_kernel(DecodeParam
 
 int64_t partial_rows(const bsa_fp8_decode_dims& d) { return (int64_t)d.batch * d.s_q * d.num_heads_q; }
 
+// Static checks shared by the split-list entry points; sets *grid (decode
+// workgroups) and returns BSA_OK, or the first error found.
+int validate(const void* q, const void* kv_cache, const int32_t* indices, const bsa_fp8_decode_dims* dims,
+             int num_splits, const void* out, int64_t* grid) {
+  if (dims == nullptr) return BSA_ERR_NULL_POINTER;
+  const bsa_fp8_decode_dims d = *dims;
+  if (d.batch < 0 || d.s_q < 0 || d.num_heads_q <= 0 || d.topk <= 0 || d.num_pages < 0) return BSA_ERR_SIZE;
+  if (d.num_heads_q % 64 != 0) return BSA_ERR_GQA;
+  if (num_splits < 1 || num_splits > kMaxSplits) return BSA_ERR_SIZE;
+  const int nblocks_all = (d.topk + kBlock - 1) / kBlock;
+  const int bps = (nblocks_all + num_splits - 1) / num_splits;
+  if ((int64_t)bps * kBlock > kMaxTopk) return BSA_ERR_TOO_LARGE;  // a part's row list must fit in LDS
+  if (d.page_size <= 0) return BSA_ERR_PAGE_SIZE;
+  if (!bsa::finite_float(d.softmax_scale)) return BSA_ERR_SOFTMAX_SCALE;
+  const int nw = d.num_heads_q % 128 == 0 ? 8 : 4;  // 16 heads per wave
+  const int64_t g = (int64_t)d.batch * d.s_q * (d.num_heads_q / (16 * nw)) * num_splits;
+  if (g > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
+  if ((int64_t)d.num_pages * d.page_size > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;  // 32-bit row ids
+  if (num_splits > 1 && partial_rows(d) > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
+  *grid = g;
+  if (g == 0) return BSA_OK;
+  if (q == nullptr || kv_cache == nullptr || indices == nullptr || out == nullptr) return BSA_ERR_NULL_POINTER;
+  return BSA_OK;
+}
+
+// Enqueue the decode (and, for several parts, the merge) with `ws` holding
+// the partial results.
+int launch(const void* q, const void* kv_cache, const int32_t* indices, const bsa_fp8_decode_dims& d,
+           int num_splits, float* ws, void* out, float* lse, void* stream, int64_t grid) {
+  const int nblocks_all = (d.topk + kBlock - 1) / kBlock;
+  const int bps = (nblocks_all + num_splits - 1) / num_splits;
+  const int nw = d.num_heads_q % 128 == 0 ? 8 : 4;
+  DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_cache);
+  p.indices = indices;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.B = d.batch;
+  p.s_q = d.s_q;
+  p.h_q = d.num_heads_q;
+  p.topk = d.topk;
+  p.num_rows = d.num_pages * d.page_size;
+  p.score_scale = d.softmax_scale * kLog2e;
+  p.num_splits = num_splits;
+  p.blocks_per_split = bps;
+  p.opart = ws;
+  p.lpart = num_splits > 1 ? p.opart + (int64_t)num_splits * partial_rows(d) * kDimV : nullptr;
+  if (nw == 8)
+    hipLaunchKernelGGL(bsa_fp8_decode_kernel<8>, dim3((unsigned)grid), dim3(512), 0,
+                       static_cast<hipStream_t>(stream), p);
+  else
+    hipLaunchKernelGGL(bsa_fp8_decode_kernel<4>, dim3((unsigned)grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p);
+  if (num_splits > 1)
+    hipLaunchKernelGGL(bsa_fp8_decode_combine_kernel, dim3((unsigned)partial_rows(d)), dim3(128), 0,
+                       static_cast<hipStream_t>(stream), p);
+  if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
+  return BSA_OK;
+}
+
+// Partial results of bsa_fp8_sparse_decode_noalloc: a file-scope device array,
+// one copy per GPU for the life of the process.  Host code never passes its
+// name to a kernel (on the host the name is only a stand-in); it uses the
+// device address that hipGetSymbolAddress returns for the current device,
+// looked up once per device on the first call there.
+constexpr uint64_t kScratchBytes = BSA_DECODE_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(float** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BSA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return BSA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = static_cast<float*>(a);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
+// Part count for the no-allocation entry point: the library's choice, lowered
+// until the partial results fit the scratch (never below the parts a list
+// needs; validation then reports what does not fit).
+int noalloc_splits(const bsa_fp8_decode_dims& d) {
+  int n = bsa_fp8_sparse_decode_num_splits(&d);
+  const uint64_t per_part = (uint64_t)partial_rows(d) * (kDimV + 1) * 4;
+  const int nblocks = (d.topk + kBlock - 1) / kBlock;
+  const int need = (nblocks * kBlock + kMaxTopk - 1) / kMaxTopk;  // parts whose lists fit
+  while (n > 1 && n > need && (uint64_t)n * per_part > kScratchBytes) --n;
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -533,54 +633,31 @@ long long bsa_fp8_sparse_decode_workspace_bytes(const bsa_fp8_decode_dims* dims,
 int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t* indices,
                              const bsa_fp8_decode_dims* dims, int num_splits, void* workspace, void* out,
                              float* lse, void* stream) {
-  if (dims == nullptr) return BSA_ERR_NULL_POINTER;
-  const bsa_fp8_decode_dims d = *dims;
-  if (d.batch < 0 || d.s_q < 0 || d.num_heads_q <= 0 || d.topk <= 0 || d.num_pages < 0) return BSA_ERR_SIZE;
-  if (d.num_heads_q % 64 != 0) return BSA_ERR_GQA;
-  if (num_splits < 1 || num_splits > kMaxSplits) return BSA_ERR_SIZE;
-  const int nblocks_all = (d.topk + kBlock - 1) / kBlock;
-  const int bps = (nblocks_all + num_splits - 1) / num_splits;
-  if ((int64_t)bps * kBlock > kMaxTopk) return BSA_ERR_TOO_LARGE;  // a part's row list must fit in LDS
-  if (d.page_size <= 0) return BSA_ERR_PAGE_SIZE;
-  if (!bsa::finite_float(d.softmax_scale)) return BSA_ERR_SOFTMAX_SCALE;
-  const int nw = d.num_heads_q % 128 == 0 ? 8 : 4;  // 16 heads per wave
-  const int64_t grid = (int64_t)d.batch * d.s_q * (d.num_heads_q / (16 * nw)) * num_splits;
-  if (grid > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
-  if ((int64_t)d.num_pages * d.page_size > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;  // 32-bit row ids
-  if (grid == 0) return BSA_OK;
-  if (q == nullptr || kv_cache == nullptr || indices == nullptr || out == nullptr ||
-      (num_splits > 1 && workspace == nullptr))
-    return BSA_ERR_NULL_POINTER;
-  if (num_splits > 1 && partial_rows(d) > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
+  int64_t grid = 0;
+  const int st = validate(q, kv_cache, indices, dims, num_splits, out, &grid);
+  if (st != BSA_OK || grid == 0) return st;
+  if (num_splits > 1 && workspace == nullptr) return BSA_ERR_NULL_POINTER;
   if (num_splits > 1 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return BSA_ERR_SIZE;
+  return launch(q, kv_cache, indices, *dims, num_splits, static_cast<float*>(workspace), out, lse, stream, grid);
+}
 
-  DecodeParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.kv = static_cast<const uint8_t*>(kv_cache);
-  p.indices = indices;
-  p.out = static_cast<uint16_t*>(out);
-  p.lse = lse;
-  p.B = d.batch;
-  p.s_q = d.s_q;
-  p.h_q = d.num_heads_q;
-  p.topk = d.topk;
-  p.num_rows = d.num_pages * d.page_size;
-  p.score_scale = d.softmax_scale * kLog2e;
-  p.num_splits = num_splits;
-  p.blocks_per_split = bps;
-  p.opart = static_cast<float*>(workspace);
-  p.lpart = num_splits > 1 ? p.opart + (int64_t)num_splits * partial_rows(d) * kDimV : nullptr;
-  if (nw == 8)
-    hipLaunchKernelGGL(bsa_fp8_decode_kernel<8>, dim3((unsigned)grid), dim3(512), 0,
-                       static_cast<hipStream_t>(stream), p);
-  else
-    hipLaunchKernelGGL(bsa_fp8_decode_kernel<4>, dim3((unsigned)grid), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), p);
-  if (num_splits > 1)
-    hipLaunchKernelGGL(bsa_fp8_decode_combine_kernel, dim3((unsigned)partial_rows(d)), dim3(128), 0,
-                       static_cast<hipStream_t>(stream), p);
-  if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
-  return BSA_OK;
+int bsa_fp8_sparse_decode_noalloc(const void* q, const void* kv_cache, const int32_t* indices,
+                                  const bsa_fp8_decode_dims* dims, int num_splits, void* out, float* lse,
+                                  void* stream) {
+  if (dims == nullptr) return BSA_ERR_NULL_POINTER;
+  if (num_splits == 0) num_splits = noalloc_splits(*dims);
+  int64_t grid = 0;
+  const int st = validate(q, kv_cache, indices, dims, num_splits, out, &grid);
+  if (st != BSA_OK) return st;
+  if (num_splits > 1 && (uint64_t)num_splits * partial_rows(*dims) * (kDimV + 1) * 4 > (uint64_t)kScratchBytes)
+    return BSA_ERR_SCRATCH;
+  if (grid == 0) return BSA_OK;
+  float* ws = nullptr;
+  if (num_splits > 1) {
+    const int sst = scratch_address(&ws);
+    if (sst != BSA_OK) return sst;
+  }
+  return launch(q, kv_cache, indices, *dims, num_splits, ws, out, lse, stream, grid);
 }
 
 int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* indices,

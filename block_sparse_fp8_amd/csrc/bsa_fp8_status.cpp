@@ -27,6 +27,7 @@ const char* bsa_fp8_status_string(int status) {
     case BSA_ERR_SCHEDULE: return "schedule_len must equal the task count";
     case BSA_ERR_SCALE_MODE: return "unknown scale_mode";
     case BSA_ERR_QK_PRECISION: return "unknown qk_precision";
+    case BSA_ERR_SCRATCH: return "the partial results exceed the library's static decode scratch";
     default: return "unknown status";
   }
 }

@@ -91,7 +91,9 @@ typedef enum {
                                   only one of sparse_indices / sparse_seq_len   */
     BSA_ERR_SCHEDULE = 15,     /* schedule_len does not match the task count    */
     BSA_ERR_SCALE_MODE = 16,   /* scale_mode not a bsa_scale_mode               */
-    BSA_ERR_QK_PRECISION = 17  /* options->qk_precision not a bsa_qk_precision  */
+    BSA_ERR_QK_PRECISION = 17, /* options->qk_precision not a bsa_qk_precision  */
+    BSA_ERR_SCRATCH = 18       /* the partial results do not fit the library's
+                                  static scratch (BSA_DECODE_SCRATCH_BYTES)     */
 } bsa_status;
 
 /* How bsa_fp8_quantize_append computes a descale from a row's largest
@@ -410,6 +412,31 @@ int bsa_fp8_sparse_decode(const void* q, const void* kv_cache, const int32_t* in
 int bsa_fp8_sparse_decode_ex(const void* q, const void* kv_cache, const int32_t* indices,
                              const bsa_fp8_decode_dims* dims, int num_splits, void* workspace,
                              void* out, float* lse, void* stream);
+
+/*
+ * bsa_fp8_sparse_decode_noalloc -- bsa_fp8_sparse_decode_ex for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc.  The partial results live in a static
+ * device array of the library (BSA_DECODE_SCRATCH_BYTES, one per GPU, held
+ * until the process ends) instead of a caller workspace; nothing is
+ * allocated and no allocating routine is called.  The caller still passes q,
+ * kv_cache, indices, out and lse.
+ *
+ * num_splits  0 = the part count of bsa_fp8_sparse_decode_num_splits, lowered
+ *             until the partial results fit the scratch; else 1 ..
+ *             BSA_DECODE_MAX_SPLITS as for bsa_fp8_sparse_decode_ex.
+ * Errors: as for bsa_fp8_sparse_decode_ex, plus BSA_ERR_SCRATCH when
+ * num_splits * B * s_q * h_q * 513 * 4 bytes exceed BSA_DECODE_SCRATCH_BYTES
+ * (checked before any HIP call), and BSA_ERR_LAUNCH when the scratch's device
+ * address cannot be obtained.  All calls on one GPU share its scratch: calls
+ * that may run at the same time on one GPU (on different streams, or from
+ * different threads) race and must be ordered by the caller.  The first call
+ * on a device looks up the scratch's address there, with that device current.
+ */
+#define BSA_DECODE_SCRATCH_BYTES (64 * 1024 * 1024)
+int bsa_fp8_sparse_decode_noalloc(const void* q, const void* kv_cache, const int32_t* indices,
+                                  const bsa_fp8_decode_dims* dims, int num_splits, void* out,
+                                  float* lse, void* stream);
 
 /*
  * Workspace bytes bsa_fp8_sparse_decode_ex needs: 0 for num_splits == 1,

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 17):
+    for s in range(0, 19):
         assert isinstance(bsa.status_string(s), str) and bsa.status_string(s)
     assert bsa.status_string(999) == "unknown status"
 
@@ -308,6 +308,30 @@ def test_split_decode_static_validation(lib):
     assert call_ex(dd(topk=2 ** 21 + 1), 256) == st["BSA_ERR_TOO_LARGE"]
     z = ctypes.c_void_p(0)
     assert lib.bsa_fp8_sparse_decode_ex(z, z, z, ctypes.byref(dd(batch=0)), 4, z, z, z, None) == st["BSA_OK"]
+
+
+def test_noalloc_decode_static_validation(lib):
+    """The no-allocation decode rejects, before any HIP call, partial results
+    beyond its static scratch, and otherwise validates like the split decode."""
+    from block_sparse_fp8_amd import DecodeDims
+    st = status_values()
+    d = DecodeDims(batch=64, s_q=2, num_heads_q=128, topk=2048, num_pages=10, page_size=64,
+                   softmax_scale=0.0417)
+    call = lambda dims, n: lib.bsa_fp8_sparse_decode_noalloc(FAKE, FAKE, FAKE, ctypes.byref(dims), n,  # noqa: E731
+                                                             FAKE, FAKE, None)
+    per_part = 64 * 2 * 128 * 513 * 4                 # 33.6 MB: two parts exceed 64 MiB
+    assert per_part * 2 > 64 * 1024 * 1024
+    assert call(d, 2) == st["BSA_ERR_SCRATCH"]
+    assert call(d, 257) == st["BSA_ERR_SIZE"]
+    assert call(DecodeDims(batch=64, s_q=2, num_heads_q=96, topk=2048, num_pages=10, page_size=64,
+                           softmax_scale=0.0417), 2) == st["BSA_ERR_GQA"]
+    assert lib.bsa_fp8_sparse_decode_noalloc(FAKE, FAKE, FAKE, None, 2, FAKE, FAKE, None) == \
+        st["BSA_ERR_NULL_POINTER"]
+    z = ctypes.c_void_p(0)
+    # nothing to do: no launch and no scratch lookup
+    assert lib.bsa_fp8_sparse_decode_noalloc(z, z, z, ctypes.byref(DecodeDims(
+        batch=0, s_q=2, num_heads_q=128, topk=64, num_pages=10, page_size=64, softmax_scale=0.04)), 4, z, z,
+        None) == st["BSA_OK"]
 
 
 def test_split_decode_sizes(lib):
