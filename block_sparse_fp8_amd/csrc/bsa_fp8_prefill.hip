@@ -1,8 +1,9 @@
 // Block-sparse FP8 (E4M3) attention prefill over a paged KV cache, gfx950.
 //
 // One workgroup of 256 threads (4 waves) owns one (sequence, q-head, 128-query
-// tile); wave w owns queries 32w..32w+31.  Two workgroups share a CU so that
-// one's softmax (VALU) overlaps the other's matrix products.
+// tile); wave w owns queries 32w..32w+31, and each lane one query (S^T = K.Q^T
+// puts a query in every accumulator column).  Two workgroups share a CU, so
+// every SIMD runs two waves.
 //
 //   1. Active-tile compaction (hpc-ops article, "Active tile list"): each wave
 //      ballots the Q tile's uint8 mask row 64 KV tiles at a time and walks the
@@ -13,37 +14,37 @@
 //      form the same ballot runs over 64 list entries at a time (valid = a
 //      tile id inside the candidate range) and the tile id is read from the
 //      entry's lane, so tiles are visited in list order.
-//   2. Per active tile, K and V rows are gathered from the paged cache (one
-//      page-table lookup per row).  V (and, for per-token K scales, the K
-//      descales) go straight to LDS with direct-to-LDS loads, double-buffered;
-//      K goes through registers, one tile ahead.
-//   3. S^T = K . Q^T.  E4M3 -> f16 is exact (a bit shift that scales values by
-//      2^-8), so K is widened to f16 once per workgroup when it is staged in
-//      LDS and Q once in registers, and the product runs on
-//      v_mfma_f32_32x32x16_f16, whose accumulation is fp32-accurate.  (The
-//      E4M3 matrix path keeps only about 14 bits below the largest product of
-//      a dot product, which moves P across E4M3 rounding boundaries.)
-//      Computing S^T makes every lane own one query, so the running max, sum
-//      and rescale are per lane.  K rows are read in a permuted order so that
-//      the accumulator registers of lane half h hold keys h*32..h*32+31 of each
-//      64-key half of the tile, in register order.
+//   2. Per active tile, K, V and the per-token K descales go from the paged
+//      cache straight to LDS (direct-to-LDS loads; a wave's 32 rows lie in one
+//      page, so a whole tile needs one wave-uniform page base per wave).
+//   3. S^T = K.Q^T.  By default on v_mfma_f32_32x32x16_f16: E4M3 -> f16 is
+//      exact (every E4M3 value, subnormals included, is an f16 normal), K is
+//      widened once per workgroup into an f16 tile and Q once in registers,
+//      and the product accumulates like fp32.  Optionally on the E4M3 matrix
+//      path (v_mfma_f32_32x32x64_f8f6f4), which keeps fewer bits below the
+//      largest product of a dot product.  K rows are read in a permuted order
+//      so that the accumulator registers of lane half h hold keys h*32.. of
+//      each 64-key half of the tile, in register order, the P operand's layout.
 //   4. Online softmax in fp32 in the log2 domain: qscale*softmax_scale*log2(e)
-//      (and the per-tensor K descale, and 2^16 for the f16 widening) is one
-//      per-lane constant; P' = exp2(x - m + log2(p_scale)) = p_scale*exp(score
-//      - max), so the P-scale (256 by default: hpc-ops article, "FP8 Tensor
-//      Core compute: fixed P-scale quantisation"; any p_scale in (0, 448]:
-//      "Quant Block Sparse Attention", "Key parameters") costs nothing.  P' is
-//      rounded to E4M3
-//      (v_cvt_pk_fp8_f32, round to nearest even) and the row sum keeps the
-//      unrounded P'.  The accumulator rescale is skipped when no row of the
-//      wave has a new maximum (the factor is then exactly 1).
+//      (and the per-tensor K descale) is one per-lane constant; per-token K
+//      descales multiply the scores.  P' = exp2(x - m + log2(p_scale)) =
+//      p_scale*exp(score - max), so the P-scale (256 by default: hpc-ops
+//      article, "FP8 Tensor Core compute: fixed P-scale quantisation"; any
+//      p_scale in (0, 448]: "Quant Block Sparse Attention", "Key parameters")
+//      costs nothing.  P' is rounded to E4M3 (v_cvt_pk_fp8_f32, round to
+//      nearest even) and the row sum keeps the unrounded P'.
 //   5. O^T += V^T . P^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3).  V stays
 //      row-major in LDS; the transposing read ds_read_b64_tr_b8 delivers it
 //      key-major.
 //   6. Epilogue: O = O_acc * vdescale / sum(P') (the 1/p_scale is inside the
-//      sum), written as bf16; LSE = ln2 * (m + log2(sum) - log2(p_scale)).  A query whose sparse
-//      set is empty gets O = 0 and LSE = -FLT_MAX ("Quant Block Sparse
-//      Attention", "Sparse indices & PA page table").
+//      sum), written as bf16; LSE = ln2 * (m + log2(sum) - log2(p_scale)).  A
+//      query whose sparse set is empty gets O = 0 and LSE = -FLT_MAX ("Quant
+//      Block Sparse Attention", "Sparse indices & PA page table").
+//
+// The tile loop is software-pipelined inside each wave (see the comment above
+// the kernel): the products of the next tile's scores run among the current
+// tile's exponentials, and the next tile's maximum among the current tile's
+// P.V products, so that one wave keeps the matrix pipe and the VALU busy.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -69,6 +70,7 @@ constexpr float kNegFltMax = -3.402823466e+38f;
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
@@ -201,12 +203,51 @@ struct ListWalk {
   }
 };
 
+// Direct-to-LDS loads, issued through asm so that the compiler does not make
+// LDS reads of other buffers wait for them (every one is waited for
+// explicitly, by `s_waitcnt vmcnt(0)` before the barrier that publishes its
+// data).  A wave writes 64 consecutive elements (16 or 4 bytes per lane) at
+// the wave-uniform LDS address `lds`.  M0 is set here and used by nothing
+// else in the kernel.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16s(uint32_t off, uint64_t sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4s(uint32_t off, uint64_t sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// The software-pipelined tile loop.  Per active tile t (with t1, t2 the next
+// two) each wave runs two phases whose matrix products and VALU work are
+// independent, so that one wave keeps both the matrix pipe and the VALU busy:
+//   A: exponentials, E4M3 packs and row sums of S(t) (scaled and max-reduced
+//      in the previous step), interleaved block by block with the products of
+//      S(t1) = K(t1).Q^T; the registers of S(t) are freed as those of S(t1)
+//      fill.
+//   B: O *= alpha(t) and O += V(t)^T.P(t)^T, interleaved with the K descales,
+//      band mask and row maximum of S(t1), and (f16 products) the widening of
+//      K(t2) into the f16 tile.
+// Loads of a step (V(t), the K descales of t1, the raw K of t2, the page ids
+// of the tile after t2) are issued at its start and waited for before the
+// barrier that separates A from B.
 template <int QUANT, int FORM, bool QK8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bsa_fp8_prefill_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) uint8_t k16_lds[kTile * kK16Row];       // 32 KB
-  __shared__ __attribute__((aligned(16))) uint8_t v8_lds[2][kTile * kHeadDim];    // 32 KB
-  __shared__ __attribute__((aligned(16))) float ks_lds[2][kTile];                 // 1 KB
+  // K for the products: f16 chunk-major tile (32 KB: 16-byte chunk c, dims
+  // 8c..8c+7, of key row r at c*2048 + r*16) fed from an E4M3 staging tile; or
+  // (FP8 products) a ring of two E4M3 tiles.  E4M3 tiles are row-major with
+  // the 16-byte chunks of row r permuted by swz8(r).
+  constexpr int kKBytes = QK8 ? 2 * kTile * kHeadDim : kTile * kK16Row;
+  __shared__ __attribute__((aligned(16))) uint8_t kmat_lds[kKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kst_lds[QK8 ? 16 : kTile * kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint8_t v8_lds[kTile * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float ks_lds[kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -286,45 +327,41 @@ bsa_fp8_prefill_kernel(Params p) {
   const bool q_valid = tq < lq;
   const int p_wave_min = lkv - lq + m * kTile + wave * 32;  // smallest position in the wave
 
-  // Q operand (B of S^T = K.Q^T, f16 32x32x16): lane holds query `col`,
-  // head-dim elements ks*16 + hd*8 .. +7 for ks = 0..7.
-  v8h qh[8];
-  v8i q8[2];  // FP8 products: lane holds query `col`, dims ks*64 + hd*32 .. +31
+  // Q operand (B of S^T = K.Q^T): f16 products, lane holds query `col`,
+  // head-dim elements ks*16 + hd*8 .. +7 for ks = 0..7; FP8 products, dims
+  // ks*64 + hd*32 .. +31 for ks = 0..1.
+  v8h qh[QK8 ? 1 : 8];
+  v8i q8[QK8 ? 2 : 1];
+  v2i qraw[QK8 ? 1 : 8];
   float cscale = 0.0f;
-  if constexpr (QK8) {
-    if (q_valid) {
-      const int64_t qi = (int64_t)(t0 + tq) * p.q_tok_stride + (int64_t)h * p.q_head_stride;
+  {
+    const int64_t qi = (int64_t)(t0 + (q_valid ? tq : 0)) * p.q_tok_stride + (int64_t)h * p.q_head_stride;
+    if constexpr (QK8) {
       const uint8_t* qp = p.q + qi * kHeadDim + hd * 32;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) q8[ks] = *reinterpret_cast<const v8i*>(qp + ks * 64);
-      cscale = p.qscale[qi] * p.qk_scale;
+      for (int ks = 0; ks < 2; ++ks)
+        q8[ks] = q_valid ? *reinterpret_cast<const v8i*>(qp + ks * 64) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
     } else {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) q8[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  } else {
-    v2i raw[8];
-    if (q_valid) {
-      const int64_t qi = (int64_t)(t0 + tq) * p.q_tok_stride + (int64_t)h * p.q_head_stride;
       const uint8_t* qp = p.q + qi * kHeadDim + hd * 8;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) raw[ks] = *reinterpret_cast<const v2i*>(qp + ks * 16);
-      cscale = p.qscale[qi] * p.qk_scale;
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) raw[ks] = v2i{0, 0};
+      for (int ks = 0; ks < 8; ++ks) qraw[ks] = q_valid ? *reinterpret_cast<const v2i*>(qp + ks * 16) : v2i{0, 0};
     }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const v2i a = e4m3x4_to_f16x4((uint32_t)raw[ks][0]);
-      const v2i c = e4m3x4_to_f16x4((uint32_t)raw[ks][1]);
-      const v4i w = v4i{a[0], a[1], c[0], c[1]};
-      qh[ks] = __builtin_bit_cast(v8h, w);
-    }
+    if (q_valid) cscale = p.qscale[qi] * p.qk_scale;
   }
+  auto widen_q = [&]() {
+    if constexpr (!QK8) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const v2i a = e4m3x4_to_f16x4((uint32_t)qraw[ks][0]);
+        const v2i c = e4m3x4_to_f16x4((uint32_t)qraw[ks][1]);
+        qh[ks] = __builtin_bit_cast(v8h, v4i{a[0], a[1], c[0], c[1]});
+      }
+    }
+  };
   if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR) cscale *= p.kscale[0];
   // Keep the score constant strictly positive so that a masked score (-inf)
-  // maps to exp2(-inf) = 0 without a select.  With descales >= 0 this only
+  // maps to exp2(-inf) = 0 without a select.  Descales are >= 0 and the
+  // softmax scale is >= 0 (the host refuses a negative one), so this only
   // changes a zero constant, where every x is then ~1e-38 * S instead of 0.
   cscale = fmaxf(cscale, 1.17549435e-38f);
   const float vdesc = QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR ? p.vscale[0] : p.vscale[g];
@@ -335,321 +372,398 @@ bsa_fp8_prefill_kernel(Params p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[d][r] = 0.0f;
   float m_run = -INFINITY;  // running max of x = score * log2(e)
-  float l_run = 0.0f;       // this lane's half of sum(P'), P' = 2^(x - m + 8)
+  float l_run = 0.0f;       // this lane's half of sum(P'), P' = p_scale * 2^(x - m)
+  float alpha = 0.0f;       // rescale of O before the next P.V
+  float bias = 0.0f;        // log2(p_scale) - m for the exponentials
+  bool rescale = false;     // some row of the wave has a new maximum
 
-  // K operand rows: accumulator row i of block c holds key
-  // (c>>1)*64 + hi*32 + (c&1)*16 + ri with hi = (i>>2)&1, ri = (i>>3)*4 + (i&3).
-
-  // Staging roles: K through registers, one row per thread (row tid & 127,
-  // head-dim bytes 64*(tid>>7) .. +63); V by direct-to-LDS loads (wave w: rows
-  // 32w..32w+31, 8 rows of 128 bytes per instruction).
+  // ---- addresses ------------------------------------------------------------
   const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
-  const int khalf = wave >> 1;
-  v4i kreg[4];
-
-  // Loads of a tile come in three parts, spread over iterations so that no
-  // memory latency sits on the critical path:
-  //  * lookup(n): the page-table entries of tile n, issued two tiles ahead and
-  //    waited only at the top of the next iteration (the VMEM counter drains
-  //    in order, so a lookup waited right before the data loads that need it
-  //    would expose a full memory round trip every tile);
-  //  * issue_k(n): the K rows of tile n into registers, one tile ahead;
-  //  * issue_v(n): the V rows (and per-token K descales) of tile n straight
-  //    into LDS, issued after the current tile's PV so that no direct-to-LDS
-  //    load is in flight while LDS operands are read (the compiler can then
-  //    wait for exact LDS counts).
-  // Rows past the KV length are redirected to row lkv-1 (valid; every lookup
-  // index is at most (lkv-1)/page_size): their K is zeroed and their P is 0.
-  // The 32 V rows of a wave lie in one 32-aligned block, hence in one page.
-  struct PageSet {
-    int k, v, ks;
-  };
-  // (vzero keeps the V page lookup a per-lane load: a wave-uniform one is moved
-  // to a scalar register at once, which waits for every load in flight)
-  int vzero = 0;
-  asm volatile("" : "+v"(vzero));
-  // K row staged by this thread: (wave & 1) * 64 + lane.
-  auto lookup = [&](int n, int ln) -> PageSet {
-    PageSet ps;
-    ps.k = bt[min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) >> p.page_shift];
-    ps.v = bt[min(n * kTile + wave * 32 + vzero, lkv - 1) >> p.page_shift];
-    ps.ks = QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD
-                ? bt[min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) >> p.page_shift]
-                : 0;
-    return ps;
-  };
+  const int head_row = g * p.head_stride;
+  const int pmask = p.page_size - 1;
   // Byte offset of (page, slot, this kv-head) in a cache: one 32x32->64-bit
   // product per page plus 32-bit in-page arithmetic.
-  const int head_row = g * p.head_stride;
   auto row_addr = [&](const uint8_t* base, int pg, int slot) -> const uint8_t* {
     return base + (uint64_t)(uint32_t)pg * p.page_bytes + (uint32_t)(slot * p.slot_stride + head_row) * kHeadDim;
   };
-  const int pmask = p.page_size - 1;
-  // (rows past the KV length are zeroed when K is widened, not here: a select
-  // on the loaded registers would make the loads complete at once)
-  auto issue_k = [&](int n, const PageSet& ps, int ln) {
-    const int slot = min(n * kTile + (wave & 1) * 64 + ln, lkv - 1) & pmask;
-    const v4i* src = reinterpret_cast<const v4i*>(row_addr(p.kc, ps.k, slot) + khalf * 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = src[i];
+  // Page id of tile n for this wave: the 32 rows a wave loads (K, V and the
+  // K descales) lie in one 32-aligned block, hence in one page.  The row is
+  // clamped to lkv-1, so no block-table entry past the sequence's pages is
+  // read.  (vzero keeps the lookup a per-lane load: a wave-uniform one would
+  // be moved to a scalar register at once, whose wait also waits for every
+  // load in flight; the value moves to a scalar register once it has
+  // arrived.)
+  int vzero = 0;
+  asm volatile("" : "+v"(vzero));
+  struct Pages {
+    int kv;
   };
-  auto issue_v = [&](int n, int buf, const PageSet& ps, int ln) {
+  auto lookup = [&](int n, int ln) -> Pages {
+    (void)ln;
+    Pages ps;
+    ps.kv = bt[min(n * kTile + wave * 32 + vzero, lkv - 1) >> p.page_shift];
+    return ps;
+  };
+  // One E4M3 tile (K or V) of tile n into LDS at `dst` (row-major, chunks
+  // permuted by swz8): wave w loads rows 32w..32w+31, 8 rows of 128 bytes per
+  // instruction.  Rows past the KV length read row lkv-1 (finite; their P is 0).
+  // A whole tile inside the KV length: the wave's 32 rows are consecutive
+  // slots of one page, and since 128 is a multiple of the page size, every
+  // lane's offset within the page (its slot, the kv-head and its swizzled
+  // chunk) is the same for every tile: only the page base changes, a
+  // wave-uniform value in SGPRs.
+  const int drow = wave * 32 + (lane >> 3);  // tile row of the lane's first load
+  const uint32_t dma_off =
+      (uint32_t)((drow & pmask) * p.slot_stride + head_row) * kHeadDim + (uint32_t)(((lane & 7) ^ swz8(drow)) << 4);
+  const uint64_t dma_step = 8ull * (uint64_t)p.slot_stride * kHeadDim;  // 8 rows further
+  auto dma_tile = [&](const uint8_t* cache, int n, int pg, uint8_t* dst, int ln) {
     const int row0 = wave * 32 + (ln >> 3);
+    const uint32_t base = lds_addr(dst) + (uint32_t)(wave * 32) * kHeadDim;
     if (n * kTile + kTile <= lkv) {
-      // Whole tile inside the KV length: the wave's 32 rows are consecutive
-      // slots of one page.
-      const uint8_t* src0 = row_addr(p.vc, ps.v, (n * kTile + row0) & pmask);
-      const uint32_t step = 8u * (uint32_t)p.slot_stride * kHeadDim;
+      const uint64_t sbase =
+          (uint64_t)(uintptr_t)cache + (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(pg) * p.page_bytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((glb_void*)(src0 + i * step + (((ln & 7) ^ swz8(row0 + i * 8)) << 4)),
-                                         (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
+      for (int i = 0; i < 4; ++i) dma16s(dma_off, sbase + i * dma_step, base + i * 8 * kHeadDim);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = row0 + i * 8;
         const int j = min(n * kTile + row, lkv - 1);
-        const uint8_t* src = row_addr(p.vc, ps.v, j & pmask) + (((ln & 7) ^ swz8(row)) << 4);
-        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&v8_lds[buf][(wave * 32 + i * 8) * kHeadDim]), 16, 0, 0);
+        dma16(row_addr(cache, pg, j & pmask) + (((ln & 7) ^ swz8(row)) << 4), base + i * 8 * kHeadDim);
       }
     }
-    if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD && wave < 2) {
-      const int slot = min(n * kTile + wave * 64 + ln, lkv - 1) & pmask;
-      const float* src = p.kscale + (uint64_t)(uint32_t)ps.ks * (p.page_bytes / kHeadDim) + (uint32_t)(slot * p.slot_stride + head_row);
-      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&ks_lds[buf][wave * 64]), 4, 0, 0);
+  };
+  // The K descales of the wave's 32 rows (lanes 0..31, one float each) from
+  // the same page: the descale array is laid out like the cache without the
+  // head dimension.  Rows past the KV length read row lkv-1.
+  auto dma_kscale = [&](int n, int pg, int ln) {
+    if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
+      const int row = n * kTile + wave * 32 + (ln & 31);
+      const uint32_t off = (uint32_t)((min(row, lkv - 1) & pmask) * p.slot_stride + head_row) * 4u;
+      const uint64_t sbase = (uint64_t)(uintptr_t)p.kscale +
+                             (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(pg) * (p.page_bytes / kHeadDim) * 4u;
+      if (ln < 32) dma4s(off, sbase, lds_addr(ks_lds) + wave * 32 * 4);
+    }
+  };
+  // f16 products: widen the staged E4M3 K tile into the f16 tile.  Thread
+  // (row tid & 127, half tid >> 7) converts dims 64*half .. +63 of its row.
+  // `part` (0..3) selects one 16-byte chunk of the thread's four.
+  auto widen_k = [&](int part, int ln) {
+    if constexpr (!QK8) {
+      const int r = (wave & 1) * 64 + ln;
+      const int half = wave >> 1;
+      const uint8_t* src = kst_lds + r * kHeadDim;
+      {
+        const int c8 = 4 * half + part;  // logical E4M3 chunk: dims 16*c8 .. +15
+        const v4i w = *reinterpret_cast<const v4i*>(src + ((c8 ^ swz8(r)) << 4));
+        const v2i a = e4m3x4_to_f16x4((uint32_t)w[0]);
+        const v2i c = e4m3x4_to_f16x4((uint32_t)w[1]);
+        const v2i d = e4m3x4_to_f16x4((uint32_t)w[2]);
+        const v2i e = e4m3x4_to_f16x4((uint32_t)w[3]);
+        *reinterpret_cast<v4i*>(kmat_lds + (2 * c8) * 2048 + r * 16) = v4i{a[0], a[1], c[0], c[1]};
+        *reinterpret_cast<v4i*>(kmat_lds + (2 * c8 + 1) * 2048 + r * 16) = v4i{d[0], d[1], e[0], e[1]};
+      }
     }
   };
 
-  // n: tile being processed (LDS buffer parity `buf` of the step); n1: the
-  // next one.  Page ids live in pg[parity of the tile's position], so no copy
-  // of a pending load result is ever needed.
-  int n = walk.next(lane);
-  int n1 = -1;
-  PageSet pg[2] = {{0, 0, 0}, {0, 0, 0}};
-  if (n >= 0) {
-    pg[0] = lookup(n, lane);
-    issue_k(n, pg[0], lane);
-    issue_v(n, 0, pg[0], lane);
-    n1 = walk.next(lane);
-    if (n1 >= 0) pg[1] = lookup(n1, lane);
-  }
+  // ---- the products S^T = K.Q^T -------------------------------------------------
+  // Accumulator row i of block c holds key (c>>1)*64 + hi*32 + (c&1)*16 + ri,
+  // hi = (i>>2)&1, ri = (i>>3)*4 + (i&3): the lane of half h then holds keys
+  // (c>>1)*64 + h*32 + (c&1)*16 + 0..15 in register order, the layout the P
+  // operand of P.V needs.  Product j of a tile is block j / kPerBlock, k-step
+  // j % kPerBlock; kop(j) reads its K operand.
+  constexpr int kPerBlock = QK8 ? 2 : 8;          // products per 32-key block
+  constexpr int kAhead = QK8 ? 2 : 3;             // operand reads ahead of their product
+  using KOp = std::conditional_t<QK8, v8i, v8h>;
+  auto kop = [&](int j, int ln, const uint8_t* kbuf) -> KOp {
+    const int c = j / kPerBlock, ks = j % kPerBlock;
+    const int lcol = ln & 31;
+    const int lhd = ln >> 5;
+    const int hi_a = (lcol >> 2) & 1;
+    const int ri_a = ((lcol >> 3) << 2) | (lcol & 3);
+    const int row = (c >> 1) * 64 + hi_a * 32 + (c & 1) * 16 + ri_a;
+    if constexpr (QK8) {
+      const uint8_t* kp = kbuf + row * kHeadDim;
+      const int sw = swz8(row);
+      const int c0 = 4 * ks + 2 * lhd;  // logical chunks c0, c0+1: dims ks*64 + 32*lhd .. +31
+      const v4i lo = *reinterpret_cast<const v4i*>(kp + ((c0 ^ sw) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(kp + (((c0 + 1) ^ sw) << 4));
+      return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return *reinterpret_cast<const v8h*>(kmat_lds + lhd * 2048 + row * 16 + ks * 4096);
+    }
+  };
+  auto mfma_qk = [&](const KOp& a, int ks, const v16f& acc) -> v16f {
+    if constexpr (QK8) return mfma_f8(a, q8[ks], acc);
+    else return mfma_f16(a, qh[ks], acc);
+  };
+  // All four blocks of a tile with no other work (the prologue).
+  auto qk_tile = [&](v16f* out, int ln, const uint8_t* kbuf) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kPerBlock; ++ks) acc = mfma_qk(kop(c * kPerBlock + ks, ln, kbuf), ks, acc);
+      out[c] = acc;
+    }
+  };
 
-  // One active tile; BUF is the LDS buffer holding its V (and K descales).
-  auto tile_step = [&](auto buf_tag) {
-    constexpr int buf = decltype(buf_tag)::value;
-    // Lane-derived offsets are recomputed from an opaque copy of the lane id
-    // every tile instead of being held in registers across the loop.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+  // ---- per-block softmax pieces ------------------------------------------------
+  // Scale + band mask + maximum of one block of S (in place); returns the
+  // block's partial maximum of the unscaled-by-cscale score.
+  // The K descales of block c (per-token K scales), read ahead of their use.
+  auto ks_read = [&](int c, int ln) -> v16f {
+    v16f k;
+    if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
+      const float* ksp = &ks_lds[(c >> 1) * 64 + (ln >> 5) * 32 + (c & 1) * 16];
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const v4f t = *reinterpret_cast<const v4f*>(ksp + r);
+        k[r] = t[0];
+        k[r + 1] = t[1];
+        k[r + 2] = t[2];
+        k[r + 3] = t[3];
+      }
+    }
+    return k;
+  };
+  auto prep_block = [&](v16f& sb, const v16f& kd, int c, int n, int ln) -> float {
     const int lhd = ln >> 5;
     const int lcol = ln & 31;
-    const int krow = (wave & 1) * 64 + ln;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // k16 and the other V buffer are no longer read; this tile's V is in LDS
-    // Widen this tile's K to f16 in LDS.  Layout is chunk-major: the 16-byte
-    // chunk c (head-dim elements 8c..8c+7) of key row r sits at c*2048 + r*16.
-    if (n * kTile + krow >= lkv) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kreg[i] = v4i{0, 0, 0, 0};
-    }
-    if constexpr (QK8) {
-      // E4M3 kept as is, chunk-major: 16-byte chunk c (dims 16c..16c+15) of
-      // key row r at c*2048 + r*16.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i*>(k16_lds + (4 * khalf + i) * 2048 + krow * 16) = kreg[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v2i a = e4m3x4_to_f16x4((uint32_t)kreg[i][0]);
-        const v2i c = e4m3x4_to_f16x4((uint32_t)kreg[i][1]);
-        const v2i d = e4m3x4_to_f16x4((uint32_t)kreg[i][2]);
-        const v2i e = e4m3x4_to_f16x4((uint32_t)kreg[i][3]);
-        const int chunk = 8 * khalf + 2 * i;
-        *reinterpret_cast<v4i*>(k16_lds + chunk * 2048 + krow * 16) = v4i{a[0], a[1], c[0], c[1]};
-        *reinterpret_cast<v4i*>(k16_lds + (chunk + 1) * 2048 + krow * 16) = v4i{d[0], d[1], e[0], e[1]};
-      }
-    }
-    __syncthreads();  // k16 ready
-    if (n1 >= 0) issue_k(n1, pg[buf ^ 1], ln);
-    const int n2 = n1 >= 0 ? walk.next(ln) : -1;
-    if (n2 >= 0) pg[buf] = lookup(n2, ln);
-
-    // ---- S^T = K . Q^T (f16 operands, fp32 accumulation) ------------------
-    // k-step outer, 32-key block inner: four independent accumulation chains,
-    // and the operands of step ks+1 are read from LDS before the products of
-    // step ks are issued, so LDS latency hides behind the matrix pipe.
-    v16f s[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[c][r] = 0.0f;
-    if constexpr (QK8) {
-      // FP8 products (v_mfma_f32_32x32x64_f8f6f4): two k-steps of 64 dims;
-      // lane half h reads dims ks*64 + 32h .. +31 of its key row (chunks
-      // 4ks + 2h and 4ks + 2h + 1).
-      const int hi_a = (lcol >> 2) & 1;
-      const int ri_a = ((lcol >> 3) << 2) | (lcol & 3);
-      const uint8_t* kp = k16_lds + 2 * lhd * 2048 + (hi_a * 32 + ri_a) * 16;
-      auto kread = [&](int c, int ks) -> v8i {
-        const uint8_t* a = kp + ((c >> 1) * 64 + (c & 1) * 16) * 16 + ks * 4 * 2048;
-        const v4i lo = *reinterpret_cast<const v4i*>(a);
-        const v4i hi = *reinterpret_cast<const v4i*>(a + 2048);
-        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      v8i ka[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) ka[x] = kread(x & 3, x >> 2);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) s[x & 3] = mfma_f8(ka[x], q8[x >> 2], s[x & 3]);
-    } else {
-      const int hi_a = (lcol >> 2) & 1;
-      const int ri_a = ((lcol >> 3) << 2) | (lcol & 3);
-      const uint8_t* kp = k16_lds + lhd * 2048 + (hi_a * 32 + ri_a) * 16;
-      auto kaddr = [&](int c, int ks) { return kp + ((c >> 1) * 64 + (c & 1) * 16) * 16 + ks * 4096; };
-      v8h acur[4], anxt[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acur[c] = *reinterpret_cast<const v8h*>(kaddr(c, 0));
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (ks < 7) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) anxt[c] = *reinterpret_cast<const v8h*>(kaddr(c, ks + 1));
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) s[c] = mfma_f16(acur[c], qh[ks], s[c]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acur[c] = anxt[c];
-      }
-      // Keep four operand reads in flight ahead of the matrix products.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // DS read
-#pragma unroll
-      for (int k = 0; k < 14; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Lane holds, for its query, keys key(c, r) = (c>>1)*64 + hd*32 + (c&1)*16 + r.
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float* ksp = &ks_lds[buf][(c >> 1) * 64 + lhd * 32 + (c & 1) * 16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[c][r] *= ksp[r];
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int r = 0; r < 16; ++r) sb[r] *= kd[r];
     }
     const bool band = (p.causal && n * kTile + kTile - 1 > p_wave_min) || (n * kTile + kTile > lkv);
     if (band) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = n * kTile + (c >> 1) * 64 + lhd * 32 + (c & 1) * 16 + r;
-          const bool ok = j < lkv && (!p.causal || j <= p_wave_min + lcol);
-          s[c][r] = ok ? s[c][r] : -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int j = n * kTile + (c >> 1) * 64 + lhd * 32 + (c & 1) * 16 + r;
+        const bool ok = j < lkv && (!p.causal || j <= p_wave_min + lcol);
+        sb[r] = ok ? sb[r] : -INFINITY;
+      }
     }
-
-    // ---- online softmax ------------------------------------------------------
-    // row max as a tree (eight independent partial maxima)
-    float pm[8];
-#pragma unroll
-    for (int q8 = 0; q8 < 8; ++q8) {
-      const int c = q8 >> 1, r0 = (q8 & 1) * 8;
-      pm[q8] = max3f(max3f(s[c][r0], s[c][r0 + 1], s[c][r0 + 2]), max3f(s[c][r0 + 3], s[c][r0 + 4], s[c][r0 + 5]),
-                     fmaxf(s[c][r0 + 6], s[c][r0 + 7]));
-    }
-    float tmax = fmaxf(max3f(pm[0], pm[1], pm[2]), max3f(pm[3], pm[4], max3f(pm[5], pm[6], pm[7])));
-    {
-      // other lane half (keys of the other 32-row halves): v_permlane32_swap
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
+    const float a = max3f(max3f(sb[0], sb[1], sb[2]), max3f(sb[3], sb[4], sb[5]), max3f(sb[6], sb[7], sb[8]));
+    const float b2 = max3f(max3f(sb[9], sb[10], sb[11]), max3f(sb[12], sb[13], sb[14]), sb[15]);
+    return fmaxf(a, b2);
+  };
+  // New running maximum from the four blocks' partial maxima (both lane
+  // halves): sets alpha, bias and rescale.
+  auto update_max = [&](float tmax) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float tmax_x = tmax == -INFINITY ? -INFINITY : tmax * cscale;
     const float m_new = fmaxf(m_run, tmax_x);
     const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);  // exp2(-inf) = 0
-    const float bias = p.pscale_log2 - m_safe;
-    const bool rescale = __ballot(m_new != m_run) != 0;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_safe);  // exp2(-inf) = 0
+    bias = p.pscale_log2 - m_safe;
+    rescale = __ballot(m_new != m_run) != 0;
     m_run = m_new;
-
-    v8i pk[2];
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  };
+  // P' = exp2(s*cscale + bias) of one block: its partial row sum, and its
+  // E4M3 codes into the P operand (bytes (c&1)*16 + r of P.V step c>>1).
+  // Masked scores are -inf and cscale > 0, so their P' is exactly 0.
+  auto exp_block = [&](const v16f& sb, int c, v8i* pk) -> float {
+    float ls = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        // masked scores are -inf and cscale > 0, so their P' is exactly 0
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[c][r], cscale, bias));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 1], cscale, bias));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 2], cscale, bias));
-        const float e3 = __builtin_amdgcn_exp2f(fmaf(s[c][r + 3], cscale, bias));
-        ls[r >> 2] += (e0 + e1) + (e2 + e3);
-        // bytes (c&1)*16 + r .. +3 of the P operand of PV step c>>1
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-        pk[c >> 1][(c & 1) * 4 + (r >> 2)] = w;
-      }
+    for (int r = 0; r < 16; r += 4) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sb[r], cscale, bias));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sb[r + 1], cscale, bias));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(sb[r + 2], cscale, bias));
+      const float e3 = __builtin_amdgcn_exp2f(fmaf(sb[r + 3], cscale, bias));
+      ls += (e0 + e1) + (e2 + e3);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+      pk[c >> 1][(c & 1) * 4 + (r >> 2)] = w;
     }
-    if (rescale) {
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-    }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return ls;
+  };
 
-    // ---- O^T += V^T . P^T ----------------------------------------------------
-    // Transposing read: in each 16-lane group, source lane 2k+q addresses key
-    // row (step*64 + half*32 + 8*rr + k) at head-dim column base + 8q; result
-    // lane i then holds column base + i for those 8 keys.
-    // Rows sp*64 + half*32 + 8*rr + kk all share this lane's chunk swizzle, so
-    // one base per head-dim block d serves the whole tile.
+  // O^T += V^T . P^T for 32 output dims (block d), both 64-key steps.
+  // Transposing read: in each 16-lane group, source lane 2k+q addresses key
+  // row (step*64 + half*32 + 8*rr + k) at head-dim column base + 8q; result
+  // lane i then holds column base + i for those 8 keys.  Rows sp*64 +
+  // half*32 + 8*rr + kk all share this lane's chunk swizzle, so one base per
+  // block serves the whole tile.
+  auto vread = [&](int x, int ln) -> v8i {  // x = sp*4 + d
     const int grp = ln >> 4;
     const int kk = (ln & 15) >> 1;
     const int half = grp >> 1;
     const int csw = (grp & 1) ^ kk ^ (half << 2);  // logical chunk 2d + (grp&1), swizzled
-    const uint8_t* vrow0 = v8_lds[buf] + (half * 32 + kk) * kHeadDim + 8 * (ln & 1);
-    auto vread = [&](int x) -> v8i {  // x = sp*4 + d
-      const uint8_t* vp = vrow0 + (((2 * (x & 3)) ^ csw) << 4) + (x >> 2) * 64 * kHeadDim;
-      v8i a;
+    const uint8_t* vp = v8_lds + (half * 32 + kk) * kHeadDim + 8 * (ln & 1) + (((2 * (x & 3)) ^ csw) << 4) +
+                        (x >> 2) * 64 * kHeadDim;
+    v8i a;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vp + rr * 8 * kHeadDim));
-        a[2 * rr] = t[0];
-        a[2 * rr + 1] = t[1];
-      }
-      return a;
-    };
-    {
-      // operands of the next product are read while the current one runs
-      v8i va[8];
-      va[0] = vread(0);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        if (x + 1 < 8) va[x + 1] = vread(x + 1);
-        oacc[x & 3] = mfma_f8(va[x], pk[x >> 2], oacc[x & 3]);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // DS read
-#pragma unroll
-      for (int k = 0; k < 7; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int rr = 0; rr < 4; ++rr) {
+      const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vp + rr * 8 * kHeadDim));
+      a[2 * rr] = t[0];
+      a[2 * rr + 1] = t[1];
     }
-    if (n1 >= 0) issue_v(n1, buf ^ 1, pg[buf ^ 1], ln);
+    return a;
+  };
+
+  // ---- the tile list ------------------------------------------------------------
+  // n: tile of the current step (its S is ready); n1, n2: the next two; n3 is
+  // looked up during the step.  Page ids: pg_n for n (V), pg_1 for n1 (K
+  // descales), pg_2 for n2 (K), pg_3 for n3.
+  int n = walk.next(lane);
+  if (n < 0) {
+    // no active tile: O = 0, LSE = -FLT_MAX
+    if (!q_valid) return;
+    uint16_t* op = p.out + ((int64_t)(t0 + tq) * p.Hq + h) * kHeadDim;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) *reinterpret_cast<v2i*>(op + d * 32 + 8 * r4 + 4 * hd) = v2i{0, 0};
+    if (p.lse != nullptr && hd == 0) p.lse[(int64_t)h * p.T + t0 + tq] = kNegFltMax;
+    return;
+  }
+  int n1 = walk.next(lane);
+  int n2 = n1 >= 0 ? walk.next(lane) : -1;
+  Pages pg_n = lookup(n, lane);
+  Pages pg_1 = n1 >= 0 ? lookup(n1, lane) : Pages{0};
+  Pages pg_2 = n2 >= 0 ? lookup(n2, lane) : Pages{0};
+  pg_n.kv = __builtin_amdgcn_readfirstlane(pg_n.kv);
+  pg_1.kv = __builtin_amdgcn_readfirstlane(pg_1.kv);
+  pg_2.kv = __builtin_amdgcn_readfirstlane(pg_2.kv);
+
+  // Prologue: K(n) and its descales; S(n), its scale, mask and maximum; then
+  // K(n1) into the product tile.
+  uint8_t* kslot0 = QK8 ? kmat_lds : kst_lds;  // where K(n) lands
+  dma_tile(p.kc, n, pg_n.kv, kslot0, lane);
+  dma_kscale(n, pg_n.kv, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) widen_k(j, lane);
+  __syncthreads();
+  v16f sa[4], sb[4];
+  {
+    widen_q();
+    qk_tile(sa, lane, kslot0);
+    float tm = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) tm = fmaxf(tm, prep_block(sa[c], ks_read(c, lane), c, n, lane));
+    update_max(tm);
+  }
+  __syncthreads();  // every wave is done with K(n) and the descales of n
+  if (n1 >= 0) {
+    dma_tile(p.kc, n1, pg_1.kv, QK8 ? kmat_lds + kTile * kHeadDim : kst_lds, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) widen_k(j, lane);
+    __syncthreads();
+  }
+
+  // One step: S(n) in `cur`, S(n1) into `nxt`.  FP8 products: K(n1) is in
+  // ring slot `par`, and K(n2) goes to slot par^1, which held K(n).
+  auto step = [&](v16f* cur, v16f* nxt, auto par_tag) {
+    constexpr int par = decltype(par_tag)::value;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    // the next tile and its page ids first (a mask-chunk load inside the walk
+    // is waited for at once, which must not also wait for the tile loads)
+    const int n3 = n2 >= 0 ? walk.next(ln) : -1;
+    const Pages pg_3 = n3 >= 0 ? lookup(n3, ln) : Pages{0};
+    // loads of the step: V(n), the descales of n1, K(n2)
+    dma_tile(p.vc, n, pg_n.kv, v8_lds, ln);
+    if (n1 >= 0) dma_kscale(n1, pg_1.kv, ln);
+    uint8_t* k2dst = QK8 ? kmat_lds + (par ^ 1) * kTile * kHeadDim : kst_lds;
+    if (n2 >= 0) dma_tile(p.kc, n2, pg_2.kv, k2dst, ln);
+
+    // ---- A: exponentials of S(n), products of S(n1) ------------------------
+    const uint8_t* k1 = QK8 ? kmat_lds + par * kTile * kHeadDim : kmat_lds;
+    v8i pk[2];
+    float ls = 0.0f;
+    // Block by block, so that S(n) frees its registers as S(n1) needs them;
+    // the K operands of block c+1 are read while block c computes, and the
+    // E4M3 codes and partial sum of each block are pinned in this phase (the
+    // compiler would otherwise sink the whole softmax to P.V, past the
+    // barrier).  The products run even after the last tile, on whatever the
+    // K tile holds, and are not used: an assignment on one path only would
+    // keep the old contents of `nxt` alive through the whole phase.
+    // K operands are read kAhead products ahead, through the block boundaries.
+    constexpr int kRing = kAhead + 1;
+    KOp ring[kRing];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) ring[j] = kop(j, ln, k1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kPerBlock; ++ks) {
+        const int j = c * kPerBlock + ks;
+        if (j + kAhead < 4 * kPerBlock) ring[(j + kAhead) % kRing] = kop(j + kAhead, ln, k1);
+        acc = mfma_qk(ring[j % kRing], ks, acc);
+      }
+      nxt[c] = acc;
+      ls += exp_block(cur[c], c, pk);
+      asm volatile("" : "+v"(pk[c >> 1]), "+v"(ls));
+      // interleave: each product with its operand read and a share of the softmax
+#pragma unroll
+      for (int ks = 0; ks < kPerBlock; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, QK8 ? 2 : 1, 0);      // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, QK8 ? 24 : 6, 0);     // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = l_run * (rescale ? alpha : 1.0f) + ls;
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // K(n1) no longer read; V(n), descales of n1 and K(n2) are in LDS
+
+    // ---- B: O *= alpha, O += V(n) P(n); maximum of S(n1); widen K(n2) -------
+    // Per 32-dim output block d: its two products (operands read one block
+    // ahead), then, while they run, the next block's V operands and rescale,
+    // a quarter of the widening of K(n2), and the scale, mask and maximum of
+    // block d of S(n1).  The rescale factor is
+    // 1 when no row has a new maximum; the widening also runs after the last
+    // tiles, on stale data that no product reads.
+    const float sc = rescale ? alpha : 1.0f;
+    v8i va0 = vread(0, ln), va1 = vread(4, ln);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[0][r] *= sc;
+    float tm = -INFINITY;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      oacc[d] = mfma_f8(va0, pk[0], oacc[d]);
+      oacc[d] = mfma_f8(va1, pk[1], oacc[d]);
+      {
+        const v16f kd = ks_read(d, ln);  // dead before the next block's V operands are read
+        widen_k(d, ln);
+        tm = fmaxf(tm, prep_block(nxt[d], kd, d, n1, ln));
+      }
+      if (d < 3) {
+        va0 = vread(d + 1, ln);
+        va1 = vread(5 + d, ln);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d + 1][r] *= sc;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (n1 >= 0) update_max(tm);
+    __syncthreads();  // V(n) and the descales no longer read; K(n2) is ready
     n = n1;
     n1 = n2;
+    n2 = n3;
+    pg_n = pg_1;
+    pg_1 = pg_2;
+    pg_2 = pg_3;
+    // the K/V page id is wave-uniform and its load has completed (it was
+    // waited for before the barrier): keep it in a scalar register
+    pg_2.kv = __builtin_amdgcn_readfirstlane(pg_2.kv);
   };
-  while (n >= 0) {
-    tile_step(std::integral_constant<int, 0>{});
+  while (true) {
+    step(sa, sb, std::integral_constant<int, 1>{});
     if (n < 0) break;
-    tile_step(std::integral_constant<int, 1>{});
+    step(sb, sa, std::integral_constant<int, 0>{});
+    if (n < 0) break;
   }
 
   // ---- epilogue ------------------------------------------------------------
