@@ -529,7 +529,7 @@ bsa_fp8_prefill_kernel(Params p) {
     }
     return k;
   };
-  auto prep_block = [&](v16f& sb, const v16f& kd, int c, int n, int ln) -> float {
+  auto prep_block = [&](v16f& sb, const v16f& kd, int c, int n, int ln, float run_max) -> float {
     const int lhd = ln >> 5;
     const int lcol = ln & 31;
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
@@ -547,7 +547,7 @@ bsa_fp8_prefill_kernel(Params p) {
     }
     const float a = max3f(max3f(sb[0], sb[1], sb[2]), max3f(sb[3], sb[4], sb[5]), max3f(sb[6], sb[7], sb[8]));
     const float b2 = max3f(max3f(sb[9], sb[10], sb[11]), max3f(sb[12], sb[13], sb[14]), sb[15]);
-    return fmaxf(a, b2);
+    return max3f(a, b2, run_max);
   };
   // New running maximum from the four blocks' partial maxima (both lane
   // halves): sets alpha, bias and rescale.
@@ -645,7 +645,7 @@ bsa_fp8_prefill_kernel(Params p) {
     qk_tile(sa, lane, kslot0);
     float tm = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) tm = fmaxf(tm, prep_block(sa[c], ks_read(c, lane), c, n, lane));
+    for (int c = 0; c < 4; ++c) tm = prep_block(sa[c], ks_read(c, lane), c, n, lane, tm);
     update_max(tm);
   }
   __syncthreads();  // every wave is done with K(n) and the descales of n
@@ -720,11 +720,12 @@ bsa_fp8_prefill_kernel(Params p) {
 
     // ---- B: O *= alpha, O += V(n) P(n); maximum of S(n1); widen K(n2) -------
     // Per 32-dim output block d: its two products (operands read one block
-    // ahead), then, while they run, the next block's V operands and rescale,
-    // a quarter of the widening of K(n2), and the scale, mask and maximum of
-    // block d of S(n1).  The rescale factor is
-    // 1 when no row has a new maximum; the widening also runs after the last
-    // tiles, on stale data that no product reads.
+    // ahead), then, while they run, a quarter of the widening of K(n2), the
+    // scale, mask and maximum of block d of S(n1), and the next block's V
+    // operands and rescale.  The widening also runs after the last tiles, on
+    // stale data that no product reads.
+    // (the factor is exactly 1 when no row of the wave has a new maximum;
+    // multiplying anyway keeps the phase free of branches)
     const float sc = rescale ? alpha : 1.0f;
     v8i va0 = vread(0, ln), va1 = vread(4, ln);
 #pragma unroll
@@ -737,7 +738,7 @@ bsa_fp8_prefill_kernel(Params p) {
       {
         const v16f kd = ks_read(d, ln);  // dead before the next block's V operands are read
         widen_k(d, ln);
-        tm = fmaxf(tm, prep_block(nxt[d], kd, d, n1, ln));
+        tm = prep_block(nxt[d], kd, d, n1, ln, tm);
       }
       if (d < 3) {
         va0 = vread(d + 1, ln);
