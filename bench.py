@@ -31,6 +31,8 @@ TILE = 128
 FLOP_PER_TILE = 4 * TILE * TILE * TILE          # 8,388,608
 KV_BYTES_PER_TILE = 2 * TILE * TILE             # 32,768
 PEAK_FP8_TFLOPS = 5000.0                        # MI355X dense FP8 MFMA
+PEAK_F16_TFLOPS = 2500.0                        # MI355X dense f16 / bf16 MFMA
+PEAK_CLOCK_GHZ = 2.4                            # the clock both peaks are quoted at
 PEAK_HBM_GBPS = 8000.0
 METRIC = "effective FP8 TFLOPS (active tiles) + prefill tokens/s; % of FP8 MFMA peak"
 _CSRC = os.path.join(ROOT, "block_sparse_fp8_amd", "csrc")
@@ -71,6 +73,61 @@ def recorded_traffic(workload, op="prefill"):
     """HBM bytes (read + written) per launch from the record, or None."""
     rec = traffic_record(workload, op)
     return None if rec is None else rec["hbm_bytes_per_launch"]
+
+
+def qk_ceiling_tflops(qk):
+    """Matrix-core ceiling of one tile's instruction mix: Q.K^T and P.V carry
+    equal FLOP; with Q.K^T on f16 MFMA (half the FP8 rate) the mix tops out at
+    1 / (0.5 / 2500 + 0.5 / 5000) = 3333 TFLOP/s."""
+    if qk == "fp8":
+        return PEAK_FP8_TFLOPS
+    return 1.0 / (0.5 / PEAK_F16_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
+
+
+def _clock_key(workload, qk):
+    return f"clock:{workload}:{'f16' if qk == 'default' else qk}"
+
+
+def clock_record(workload, qk):
+    """The shader clock measured for this kernel source and workload, or None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[_clock_key(workload, qk)]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash("prefill"):
+        return None
+    return rec
+
+
+def ingest_clock(workload, qk, directory, command):
+    """Record the prefill kernel's mean shader clock from a GRBM_GUI_ACTIVE pass:
+    the counter sums busy cycles over the XCDs, so one XCD's cycles divided by
+    the dispatch's own start-to-end time is the clock it ran at."""
+    kname = KERNELS["prefill"][1]
+    nxcc = 8
+    for path in glob.glob(os.path.join(directory, "**", "*agent_info.csv"), recursive=True):
+        for row in csv.DictReader(open(path)):
+            if row.get("Name", "").startswith("gfx") and row.get("Num_Xcc"):
+                nxcc = int(row["Num_Xcc"])
+    ghz, ns = [], []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(path)):
+            if kname in row["Kernel_Name"] and row["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+                ghz.append(float(row["Counter_Value"]) / nxcc / dur)
+                ns.append(dur)
+    rec = {"kernel_source_sha256": kernel_source_hash("prefill"), "num_xcc": nxcc,
+           "dispatches": len(ghz), "clock_ghz_mean": sum(ghz) / len(ghz),
+           "clock_ghz_min": min(ghz), "clock_ghz_max": max(ghz),
+           "dispatch_ns_mean": sum(ns) / len(ns), "command": command}
+    try:
+        allrec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[_clock_key(workload, qk)] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+    print(json.dumps(rec))
 
 
 def _counter_means(directory, kernel_substr):
@@ -401,8 +458,8 @@ def cpu_baseline_decode(p, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sparse16k")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -430,6 +487,9 @@ def main():
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="record HBM traffic of --op's kernel on --workload from rocprofv3 counter CSV "
                          "directories and exit")
+    ap.add_argument("--ingest-clock", metavar="GRBM_DIR",
+                    help="record the prefill kernel's shader clock from a rocprofv3 --pmc GRBM_GUI_ACTIVE "
+                         "run of the same workload and --qk")
     ap.add_argument("--ingest-command", default="", help="command line recorded with --ingest-counters")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB (x3), for calibrating FETCH_SIZE/WRITE_SIZE")
@@ -442,6 +502,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copied_bytes": COPY_BYTES, "copies": 3}))
+        return
+    if args.ingest_clock:
+        ingest_clock(args.workload, args.qk, args.ingest_clock, args.ingest_command)
         return
     if args.ingest_counters:
         ingest_counters(args.workload, *args.ingest_counters, command=args.ingest_command, op=args.op)
@@ -548,7 +611,9 @@ def main():
         flushed_ms = round(float(np.median([s.elapsed_time(e) for s, e in fe])), 4)
         del flush
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
-    rec = traffic_record(p.cfg.name) if args.form == "mask" and not args.schedule else None
+    # the traffic record is taken on the default launch (mask form, f16 Q.K^T)
+    recorded = args.form == "mask" and not args.schedule and args.qk != "fp8"
+    rec = traffic_record(p.cfg.name) if recorded else None
     dram_read_gbps = None
     if rec is not None:
         dram_read_gbps = round(rec["fetch_kib_per_launch"] * 1024 * rec["fetch_scale"]
@@ -557,6 +622,8 @@ def main():
     kv_bytes = n_act * (KV_BYTES_PER_TILE + (TILE * 4 if p.quant_type == 1 else 0))
     tflops = flop / (wall / args.steps) / 1e12
     achieved = flop / avg_kernel_s / 1e12
+    crec = clock_record(p.cfg.name, args.qk) if args.form == "mask" and not args.schedule else None
+    clk = None if crec is None else crec["clock_ghz_mean"]
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -568,13 +635,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "dtype": ("fp8_e4m3 MFMA for Q.K^T and P.V, fp32 accumulate, bf16 out" if args.qk == "fp8" else
+                  "Q.K^T on f16 MFMA (E4M3 codes widened exactly to f16), P.V on fp8_e4m3 MFMA, "
+                  "fp32 accumulate, bf16 out"),
         "data": "synthetic (seeded N(0,1) quantised to E4M3, random paging and block mask)",
         "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "active_tiles": n_act,
                    "q_tokens": T, "causal": bool(p.causal), "sparsity_form": args.form,
                    "schedule_pre_pass": bool(args.schedule), "qk_precision": args.qk},
         "tokens_per_s": round(T / (wall / args.steps), 1),
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+        # the matrix-core ceiling of this instruction mix, and both peaks scaled
+        # to the shader clock measured for this kernel source (GRBM_GUI_ACTIVE)
+        "mix_ceiling_tflops": round(qk_ceiling_tflops(args.qk), 1),
+        "pct_mix_ceiling": round(100 * achieved / qk_ceiling_tflops(args.qk), 2),
+        "measured_clock_ghz": None if clk is None else round(clk, 3),
+        "pct_fp8_peak_at_measured_clock": None if clk is None else
+            round(100 * achieved / (PEAK_FP8_TFLOPS * clk / PEAK_CLOCK_GHZ), 2),
+        "pct_mix_ceiling_at_measured_clock": None if clk is None else
+            round(100 * achieved / (qk_ceiling_tflops(args.qk) * clk / PEAK_CLOCK_GHZ), 2),
         "useful_tflops": round(pairs * 4 * TILE / (wall / args.steps) / 1e12, 2),
         "kv_gbps_logical": round(kv_bytes / (wall / args.steps) / 1e9, 1),
         "kernel_ms_min": round(float(kernel_ms.min()), 4),
@@ -585,8 +663,7 @@ def main():
         "kv_gbps_dram": dram_read_gbps,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": recorded_traffic(p.cfg.name)
-                     if args.form == "mask" and not args.schedule else None},
+                     "traffic": recorded_traffic(p.cfg.name) if recorded else None},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, n_act, args.cpu_budget)

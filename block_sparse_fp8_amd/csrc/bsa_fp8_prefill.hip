@@ -364,7 +364,6 @@ bsa_fp8_prefill_kernel(Params p) {
   // softmax scale is >= 0 (the host refuses a negative one), so this only
   // changes a zero constant, where every x is then ~1e-38 * S instead of 0.
   cscale = fmaxf(cscale, 1.17549435e-38f);
-  const float vdesc = QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR ? p.vscale[0] : p.vscale[g];
 
   v16f oacc[4];
 #pragma unroll
@@ -389,17 +388,18 @@ bsa_fp8_prefill_kernel(Params p) {
   // Page id of tile n for this wave: the 32 rows a wave loads (K, V and the
   // K descales) lie in one 32-aligned block, hence in one page.  The row is
   // clamped to lkv-1, so no block-table entry past the sequence's pages is
-  // read.  (vzero keeps the lookup a per-lane load: a wave-uniform one would
-  // be moved to a scalar register at once, whose wait also waits for every
-  // load in flight; the value moves to a scalar register once it has
-  // arrived.)
-  int vzero = 0;
-  asm volatile("" : "+v"(vzero));
+  // read.  (An opaque zero in a vector register keeps the lookup a per-lane
+  // load: a wave-uniform one would be moved to a scalar register at once,
+  // whose wait also waits for every load in flight; the value moves to a
+  // scalar register once it has arrived.  The zero is made afresh for each
+  // lookup so that no register holds it across the loop.)
   struct Pages {
     int kv;
   };
   auto lookup = [&](int n, int ln) -> Pages {
     (void)ln;
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
     Pages ps;
     ps.kv = bt[min(n * kTile + wave * 32 + vzero, lkv - 1) >> p.page_shift];
     return ps;
@@ -608,16 +608,27 @@ bsa_fp8_prefill_kernel(Params p) {
   // n: tile of the current step (its S is ready); n1, n2: the next two; n3 is
   // looked up during the step.  Page ids: pg_n for n (V), pg_1 for n1 (K
   // descales), pg_2 for n2 (K), pg_3 for n3.
+  // The stores at the end derive the lane's query and half again from a
+  // fresh lane id (an opaque instruction, not a copy of `lane`), so that
+  // neither stays live, in registers or spilled, across the tile loop.
+  auto fresh_lane = []() -> int {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+  };
   int n = walk.next(lane);
   if (n < 0) {
     // no active tile: O = 0, LSE = -FLT_MAX
-    if (!q_valid) return;
-    uint16_t* op = p.out + ((int64_t)(t0 + tq) * p.Hq + h) * kHeadDim;
+    const int eln = fresh_lane();
+    const int etq = m * kTile + wave * 32 + (eln & 31);
+    const int ehd = eln >> 5;
+    if (etq >= lq) return;
+    uint16_t* op = p.out + ((int64_t)(t0 + etq) * p.Hq + h) * kHeadDim;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) *reinterpret_cast<v2i*>(op + d * 32 + 8 * r4 + 4 * hd) = v2i{0, 0};
-    if (p.lse != nullptr && hd == 0) p.lse[(int64_t)h * p.T + t0 + tq] = kNegFltMax;
+      for (int r4 = 0; r4 < 4; ++r4) *reinterpret_cast<v2i*>(op + d * 32 + 8 * r4 + 4 * ehd) = v2i{0, 0};
+    if (p.lse != nullptr && ehd == 0) p.lse[(int64_t)h * p.T + t0 + etq] = kNegFltMax;
     return;
   }
   int n1 = walk.next(lane);
@@ -769,15 +780,20 @@ bsa_fp8_prefill_kernel(Params p) {
 
   // ---- epilogue ------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!q_valid) return;
+  // (the V descale is read here too rather than kept live across the loop)
+  const int eln = fresh_lane();
+  const int etq = m * kTile + wave * 32 + (eln & 31);
+  const int ehd = eln >> 5;
+  if (etq >= lq) return;
   const bool empty = !(l_tot > 0.0f);
+  const float vdesc = QUANT == BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR ? p.vscale[0] : p.vscale[g];
   const float inv = empty ? 0.0f : vdesc / l_tot;
-  uint16_t* op = p.out + ((int64_t)(t0 + tq) * p.Hq + h) * kHeadDim;
+  uint16_t* op = p.out + ((int64_t)(t0 + etq) * p.Hq + h) * kHeadDim;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = d * 32 + 8 * r4 + 4 * hd;
+      const int d0 = d * 32 + 8 * r4 + 4 * ehd;
       const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[d][4 * r4 + 0] * inv) |
                           ((uint32_t)f32_to_bf16_rne(oacc[d][4 * r4 + 1] * inv) << 16);
       const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[d][4 * r4 + 2] * inv) |
@@ -785,8 +801,8 @@ bsa_fp8_prefill_kernel(Params p) {
       *reinterpret_cast<v2i*>(op + d0) = v2i{(int)w0, (int)w1};
     }
   }
-  if (p.lse != nullptr && hd == 0) {
-    p.lse[(int64_t)h * p.T + t0 + tq] = empty ? kNegFltMax : (m_run + log2f(l_tot) - p.pscale_log2) * kLn2;
+  if (p.lse != nullptr && ehd == 0) {
+    p.lse[(int64_t)h * p.T + t0 + etq] = empty ? kNegFltMax : (m_run + log2f(l_tot) - p.pscale_log2) * kLn2;
   }
 }
 
