@@ -13,27 +13,27 @@
 // serves all heads of a query token (up to 128, 16 per wave), so every row is
 // read and dequantised once.
 //
-// Per workgroup (sequence b, query token s, 16*NW heads):
-//   prologue: every list entry goes to an LDS list (-1 for an entry that
-//      names no row: negative, or at or past num_pages * page_size), and Q of
-//      each wave's 16 heads to registers.
-//   The list is then walked 32 tokens at a time; the rows of block n+2 are
-//   fetched while block n is computed, by direct-to-LDS loads into a ring of
-//   three staging buffers (41 chunks of 16 bytes per row, spread over 16
-//   lanes), so the loop issues no other global loads and every wait is an
-//   exact count of them.
-//   A. dequantise: lane (token t, part p) converts codes 32p..32p+31 of its row
-//      (E4M3 -> fp32, times the tile's descale, -> bfloat16, round to nearest
-//      even) into a row-major bfloat16 K tile [32 tokens][576] in LDS, and
-//      copies 8 of the 64 bfloat16 values.
-//   B. S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, wave w owning heads
-//      16w..16w+15.  K rows are read in a permuted order so that each lane
-//      holds 8 consecutive tokens of one head, the layout of the P operand
-//      below.  Online softmax in the log2 domain; P is rounded to bfloat16 into
-//      an LDS buffer [heads][32 tokens], with each head's rescale factor.
-//   C. O^T += V^T . P^T: wave w owns 512/NW output dims for all heads, so each
-//      V value is read from LDS once per workgroup; V^T comes from the
-//      row-major K tile through the transposing read ds_read_b64_tr_b16.
+// Per workgroup (sequence b, query token s, 16*NW heads), the list is walked
+// 32 tokens ("a block") at a time; every global load inside the loop is a
+// direct-to-LDS load, so each wait is an exact count of them:
+//   row ids: every wave copies the 32 entries of block n+5 into a ring of six
+//      blocks in LDS (an entry is used only if it lies in the list and names a
+//      row: 0 <= entry < num_pages * page_size).
+//   staging: the rows of block n+3 go into a ring of three staging buffers
+//      (41 chunks of 16 bytes per row, 16 lanes per row).
+//   dequantise (block n+1, while block n is multiplied): E4M3 -> fp32, times
+//      the tile's descale, -> bfloat16 (round to nearest even) into one of two
+//      bfloat16 K tiles [32 tokens][576] in LDS, plus the 64 bfloat16 values.
+//   S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, wave w owning heads
+//      16w..16w+15; tokens sit in the K tile in the order those reads want, so
+//      each lane holds 8 consecutive tokens of one head, the layout of the P
+//      operand below.  Online softmax in the log2 domain with a lazily moved
+//      reference maximum; P rounded to bfloat16 into LDS.
+//   O^T += V^T . P^T: wave w owns 512/NW output dims for all heads, so each V
+//      value is read from LDS once per workgroup; V^T comes from the row-major
+//      K tile through the transposing read ds_read_b64_tr_b16.
+// Two barriers per block: before P.V (P ready) and after it (the next K tile
+// ready, the current one free).
 // Epilogue: O = O_acc / l per head, bfloat16; LSE = ln sum exp(score).  A
 // query with no valid index gets O = 0 and LSE = -FLT_MAX.
 //
@@ -59,9 +59,9 @@ constexpr int kBlock = 32;          // tokens per iteration
 constexpr int kDimK = 576;
 constexpr int kDimV = 512;
 constexpr int kRowBytes = 656;
-constexpr int kKStride = kDimK * 2 + 16;   // bytes per LDS K row (padded)
-constexpr int kMaxTopk = BSA_DECODE_MAX_TOPK;  // longest index list one workgroup holds (LDS row list)
-constexpr int kStages = 3;                 // staging ring: block n+2 loads while n computes
+constexpr int kKStride = kDimK * 2 + 32;   // bytes per LDS K row (padded: conflict-free reads)
+constexpr int kMaxTopk = BSA_DECODE_MAX_TOPK;  // longest index list one workgroup walks (interface limit)
+constexpr int kStages = 3;                 // staging ring: block n+3 loads while n+1 is dequantised
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegFltMax = -3.402823466e+38f;
@@ -126,30 +126,48 @@ __device__ __forceinline__ void dma_lds16(const void* gptr, uint32_t lds_addr) {
 // Workgroup barrier that waits for this wave's LDS operations only.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Staging of one block per wave: three rounds of 64 lanes x 16 bytes.  Chunk c
-// of a 656-byte row (41 chunks): c < 32 codes 16c..16c+15 -> lane part c/2,
-// round c%2; c = 32 the four descales -> part 0, round 2; c = 33..40 the
-// bfloat16 values -> part c-32, round 2.
+// Direct-to-LDS load of 4 bytes per active lane (lane l writes lds_addr + 4l).
+__device__ __forceinline__ void dma_lds4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
+}
+
+// Staging of one block: for each group of 4 tokens ("set") a wave issues three
+// rounds of 64 lanes x 16 bytes; lane (token tl = lane/16, part p = lane%16)
+// of round 0 fetches codes 16p..16p+15 of its row, round 1 codes
+// 256+16p..256+16p+15, round 2 the chunk 32+min(p, 8) (the four descales for
+// p = 0, the bfloat16 values for p = 1..8; parts 9..15 repeat chunk 40).  So in
+// each round a token's bytes are consecutive: codes 0..255 at 256*tl of round 0.
 constexpr int kRound = 64 * 16;
+constexpr int kRowRing = 6;        // blocks of row ids in LDS: n-1 .. n+5 around step n
+// A head keeps its reference maximum until a block's maximum exceeds it by
+// more than this (log2 units): P = 2^(x - reference) then stays below 2^8,
+// which bfloat16 and the fp32 sums hold with the same relative rounding, and
+// the accumulators are rescaled only when some head's reference moves.
+constexpr float kLazyRescale = 8.0f;
+
+// Row of token t (0..31) of a block in the LDS K tile.  The Q.K^T reads have
+// lane c of each 16 read row c (tokens 8(c/4) + c%4) for the first product and
+// row 16 + c (those tokens + 4) for the second, a pattern with no bank
+// conflicts at a row stride of 1184 bytes.
+__device__ __forceinline__ int krow(int t) { return ((t >> 2) & 1) * 16 + (t >> 3) * 4 + (t & 3); }
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p) {
-  constexpr int kThreads = NW * 64;
   constexpr int kHeads = 16 * NW;          // heads per workgroup
   constexpr int kDW = kDimV / NW;          // output dims per wave in P.V
   constexpr int kDB = kDW / 16;            // 16-dim blocks per wave
-  constexpr int kTokThreads = kThreads / kBlock;  // lanes per token in the gather (16 or 8)
-  static_assert(kTokThreads == 16 || kTokThreads == 8, "gather layout");
-  // load rounds per block and wave (three per 16-lane part)
-  constexpr int kRoundsPerBlock = kTokThreads == 16 ? 3 : 6;
-  constexpr int kWaveStage = kRoundsPerBlock * kRound;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBlock * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t p_lds[kHeads * kBlock];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[kStages * NW * kWaveStage];
-  __shared__ __attribute__((aligned(16))) int32_t rows_lds[kMaxTopk];
+  constexpr int kSets = 8 / NW;            // groups of 4 tokens each wave stages and dequantises
+  constexpr int kWaveStage = kSets * 3 * kRound;
+  constexpr int kStageBytes = NW * kWaveStage;  // one block
+  constexpr int kKTile = kBlock * kKStride;
+  constexpr int kLoadsPerStep = 1 + 3 * kSets;  // direct-to-LDS loads a wave issues per block
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2 * kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[4 * kHeads * 16];  // [token group][head][8 tokens]
+  __shared__ __attribute__((aligned(16))) int32_t rows_lds[kRowRing * kBlock];
   __shared__ float alpha_lds[kHeads];
   __shared__ float l_lds[kHeads];
-  __shared__ int rescale_lds;   // set when any head of the block needs its O rescaled
+  __shared__ int rescale_lds[2];  // per step parity: some head's reference maximum moved
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,55 +188,121 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   const int nblocks_all = p.num_rows > 0 ? (p.topk + kBlock - 1) / kBlock : 0;
   const int n_begin = split * p.blocks_per_split;
   const int nblocks = max(0, min(nblocks_all - n_begin, p.blocks_per_split));
+  // entries of this part: positions 0 .. lim-1 of idx_row
+  const int32_t* idx_row = p.indices + (int64_t)bs * p.topk + (int64_t)n_begin * kBlock;
+  const int lim = min(p.topk - n_begin * kBlock, nblocks * kBlock);
 
-  // ---- prologue: Q to registers, every entry's cache row to LDS --------------
+  // ---- prologue: Q to registers --------------------------------------------------
   v4i qreg[18];  // B operand of S^T = K.Q^T: head 16w + c16, dims 32*ks + 8*G .. +7
   {
     const uint16_t* qp = p.q + ((int64_t)bs * p.h_q + h0 + wave * 16 + c16) * kDimK + 8 * G;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const v4i*>(qp + 32 * ks);
-    // complete here: inside the loop the only loads in flight are the staged
-    // rows, whose waits are counted exactly
+    // complete here: inside the loop the only loads in flight are the
+    // direct-to-LDS ones, whose waits are counted exactly
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qreg[ks]));
   }
-  if (nblocks > 0) {
-    const int32_t* idx_row = p.indices + (int64_t)bs * p.topk + n_begin * kBlock;
-    const int avail = p.topk - n_begin * kBlock;  // entries of the list from this part on
-    for (int k = tid; k < nblocks * kBlock; k += kThreads) {  // padded to whole blocks with -1
-      const int idx = k < avail ? idx_row[k] : -1;
-      rows_lds[k] = idx >= 0 && idx < p.num_rows ? idx : -1;
-    }
+  if (tid == 0) {
+    rescale_lds[0] = 0;
+    rescale_lds[1] = 0;
   }
-  __syncthreads();
 
-  // gather roles: token tok of a block, part (0..15 with 16 lanes per token;
-  // with 8 lanes per token each lane does the work of parts 2*part, 2*part+1)
-  const int tok = tid / kTokThreads;
-  const int part = tid % kTokThreads;
-  const int fallback_row = 0;  // loads of unused entries read row 0 (exists whenever nblocks > 0)
-  auto row_of = [&](int n) -> int { return n < nblocks ? rows_lds[n * kBlock + tok] : -1; };
-  const uint32_t stage_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage_lds) + wave * kWaveStage;
-  // Issue the loads of block n into staging buffer n % 3: the same number of
-  // load instructions (kRoundsPerBlock) for every block, so waits can count.
-  auto stage_block = [&](int n) {
-    const int row = row_of(n);
-    const uint8_t* r = p.kv + (int64_t)(row >= 0 ? row : fallback_row) * kRowBytes;
-    const uint32_t dst = stage_base + (uint32_t)(n % kStages) * (NW * kWaveStage);
-    if constexpr (kTokThreads == 16) {
-      dma_lds16(r + 32 * part, dst);
-      dma_lds16(r + 32 * part + 16, dst + kRound);
-      // chunk 32 + part (descales, then the bfloat16 values); parts 9..15 reload chunk 40
-      dma_lds16(r + kDimV + 16 * min(part, 8), dst + 2 * kRound);
-    } else {
-      // 8 lanes per token: lane part takes parts 2*part and 2*part+1 of the 16-lane layout
+  const uint32_t k_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)k_lds);
+  const uint32_t stage_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage_lds) + (uint32_t)(wave * kWaveStage);
+  const uint32_t rows_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)rows_lds);
+  // A token's entry is valid when it lies in this part and names a cache row.
+  auto valid = [&](int pos, int r) { return pos < lim && (unsigned)r < (unsigned)p.num_rows; };
+  // Row ids of block k into ring slot k % kRowRing.  Every wave loads the same
+  // 32 entries (so each can wait for its own copy); positions past the part
+  // read its last entry and are never used.
+  auto load_rows = [&](int k, int ln) {
+    const int pos = min(k * kBlock + ln, lim - 1);
+    if (ln < kBlock) dma_lds4(idx_row + pos, rows_base + (uint32_t)((k % kRowRing) * kBlock * 4));
+  };
+  // Rows of block k into staging buffer k % kStages (the same number of loads
+  // for every block, so that waits can count them; an entry that names no row
+  // loads row 0, which exists whenever there is a block).
+  auto stage_block = [&](int k, int ln) {
+    const int32_t* ring = rows_lds + (k % kRowRing) * kBlock;
+    const int pp = ln & 15;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int pp = 2 * part + h;
-        dma_lds16(r + 32 * pp, dst + (3 * h) * kRound);
-        dma_lds16(r + 32 * pp + 16, dst + (3 * h + 1) * kRound);
-        dma_lds16(r + kDimV + 16 * min(pp, 8), dst + (3 * h + 2) * kRound);
+    for (int st = 0; st < kSets; ++st) {
+      const int t = (wave * kSets + st) * 4 + (ln >> 4);
+      const int r = ring[t];
+      const uint8_t* src = p.kv + (int64_t)(valid(k * kBlock + t, r) ? r : 0) * kRowBytes;
+      const uint32_t dst = stage_base + (uint32_t)((k % kStages) * kStageBytes + st * 3 * kRound);
+      dma_lds16(src + 16 * pp, dst);
+      dma_lds16(src + 256 + 16 * pp, dst + kRound);
+      dma_lds16(src + kDimV + 16 * min(pp, 8), dst + 2 * kRound);
+    }
+  };
+  // Dequantise block k from its staging buffer into K tile k & 1: lane (tl, p)
+  // converts codes 128j + 8p .. +7 (tile j = 0..3) of its token and writes them
+  // as 16 bytes of bfloat16 at 256j + 16p of the token's row, so the 16 lanes
+  // of a token write 256 consecutive bytes per instruction; lanes p = 1..8
+  // copy the 64 bfloat16 values.  An entry that names no row was staged from
+  // row 0, which may hold anything: its K/V values are written as zeros, so
+  // that its zero probability cannot meet a NaN or infinity in the products.
+  auto dequant = [&](int k, int ln) {
+    const uint8_t* sb = stage_lds + (k % kStages) * kStageBytes + wave * kWaveStage;
+    uint8_t* kt = k_lds + (k & 1) * kKTile;
+    const int32_t* ring = rows_lds + (k % kRowRing) * kBlock;
+    const int tl = ln >> 4;
+    const int pp = ln & 15;
+#pragma unroll
+    for (int st = 0; st < kSets; ++st) {
+      const int t = (wave * kSets + st) * 4 + tl;
+      const bool ok = valid(k * kBlock + t, ring[t]);
+      const uint8_t* rb = sb + st * 3 * kRound + 256 * tl;
+      uint8_t* dst = kt + krow(t) * kKStride;
+      // every read first, then the conversions
+      v2i codes[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        codes[j] = *reinterpret_cast<const v2i*>(rb + (j >> 1) * kRound + 128 * (j & 1) + 8 * pp);
+      const v4f sc4 = *reinterpret_cast<const v4f*>(rb + 2 * kRound);
+      const v4i rope = *reinterpret_cast<const v4i*>(rb + 2 * kRound + 16 * pp);
+      // A power-of-two descale in [2^-100, 2^100] (the format's own: amax/448
+      // rounded up to a power of two) makes code * descale exact in bfloat16,
+      // and v_cvt_scalef32_pk_bf16_fp8, which applies only the scale's
+      // exponent, then gives the same bits as the fp32 product rounded to
+      // bfloat16, in one instruction per two values instead of four.  Other
+      // descales take the fp32 product; the choice is made per wave.
+      bool pow2 = true;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t su = __float_as_uint(sc4[j]);
+        pow2 = pow2 && (su & 0x807fffffu) == 0 && (su >> 23) >= 27 && (su >> 23) <= 227;
       }
+      const bool all_pow2 = __builtin_amdgcn_ballot_w64(!(ok && !pow2)) == ~0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float scale = ok ? sc4[j] : 1.0f;
+        const v2i c2 = ok ? codes[j] : v2i{0, 0};
+        uint32_t w[4];
+        if (all_pow2) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t c = (uint32_t)c2[h];
+            w[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false));
+            w[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, true));
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t c = (uint32_t)c2[h];
+            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+            w[2 * h] = pack_bf16(lo[0] * scale, lo[1] * scale);
+            w[2 * h + 1] = pack_bf16(hi[0] * scale, hi[1] * scale);
+          }
+        }
+        *reinterpret_cast<v4i*>(dst + 256 * j + 16 * pp) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      }
+      if (pp >= 1 && pp <= 8)
+        *reinterpret_cast<v4i*>(dst + 2 * kDimV + 16 * (pp - 1)) = ok ? rope : v4i{0, 0, 0, 0};
     }
   };
 
@@ -227,123 +311,100 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int hb = 0; hb < NW; ++hb) oacc[db][hb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY;  // per head (column c16 of this wave), log2 domain
-  float l_run = 0.0f;       // this lane's share of the row sum
+  float m_run = -INFINITY;  // reference maximum per head (column c16 of this wave), log2 domain
+  float l_run = 0.0f;       // this lane's share of the row sum, relative to the reference
 
+  // Per step n the loads of a wave are: the row ids of block n+5, then the
+  // rows of block n+3; the staging of block k is dequantised at step k-1.
+  // In the prologue the same order is set up for blocks 0..4 / 0..2.
   if (nblocks > 0) {
-    stage_block(0);
-    stage_block(1);
+    load_rows(0, lane);
+    load_rows(1, lane);
+    load_rows(2, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    stage_block(0, lane);
+    load_rows(3, lane);
+    stage_block(1, lane);
+    load_rows(4, lane);
+    stage_block(2, lane);
+    // block 0 has arrived once only the loads of blocks 1 and 2 remain
+    if constexpr (kLoadsPerStep == 4)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    dequant(0, lane);
   }
+  lds_barrier();  // K tile 0 and the flags are ready
 
   for (int n = 0; n < nblocks; ++n) {
+    // the loads issued two steps ago (row ids of n+3, rows of n+1) are complete
+    // once at most the previous step's remain in flight
+    if constexpr (kLoadsPerStep == 4)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
     // Lane-derived offsets are recomputed every block from an opaque copy of the
     // lane id rather than held in registers across the loop.
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    load_rows(n + 5, ln);   // ring slot of block n-1, last read in the previous step
+    stage_block(n + 3, ln);  // staging buffer of block n, dequantised in the previous step
+    if (tid == 0) rescale_lds[(n + 1) & 1] = 0;  // the next step's flag (last read in the previous step)
     const int lG = ln >> 4;
     const int lc16 = ln & 15;
-    const int ltok = (wave * 64 + ln) / kTokThreads;
-    const int lpart = (wave * 64 + ln) % kTokThreads;
-    // ---- A: dequantise block n into the K tile ------------------------------
-    // block n's loads are complete once at most block n+1's remain in flight
-    if constexpr (kRoundsPerBlock == 3)
-      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    lds_barrier();  // the previous block's K tile, P buffer and flag are no longer read
-    if (tid == 0) rescale_lds = 0;
-    {
-      const uint8_t* sb = stage_lds + (n % kStages) * (NW * kWaveStage) + wave * kWaveStage;
-      uint8_t* dst = k_lds + ltok * kKStride;
-      // An entry that names no row was staged from row 0, which may hold
-      // anything: its K/V values are written as zeros, so that its zero
-      // probability cannot meet a NaN or infinity in the P.V product.
-      const bool tok_valid = rows_lds[n * kBlock + ltok] >= 0;
-      // lane of part 0 of this token within the wave (16-lane layout: its round 2
-      // holds the four descales)
-#pragma unroll
-      for (int h = 0; h < (kTokThreads == 16 ? 1 : 2); ++h) {
-        const int pp = kTokThreads == 16 ? lpart : 2 * lpart + h;  // part in the 16-lane layout
-        const uint8_t* rb = sb + 3 * h * kRound;                 // this lane's rounds for pp
-        // the four descales: round 2 of the token's first lane (part 0)
-        const int lane0 = ln & ~(kTokThreads - 1);
-        const float scale =
-            tok_valid ? *reinterpret_cast<const float*>(sb + 2 * kRound + 16 * lane0 + 4 * (pp >> 2)) : 1.0f;
-        // A power-of-two descale in [2^-100, 2^100] (the format's own: amax/448
-        // rounded up to a power of two) makes code * descale exact in bfloat16,
-        // and v_cvt_scalef32_pk_bf16_fp8, which applies only the scale's
-        // exponent, then gives the same bits as the fp32 product rounded to
-        // bfloat16, in one instruction per two values instead of four.  Any
-        // other descale takes the fp32 product.
-        const uint32_t su = __float_as_uint(scale);
-        const bool pow2 = (su & 0x807fffffu) == 0 && (su >> 23) >= 27 && (su >> 23) <= 227;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const v4i codes = tok_valid ? *reinterpret_cast<const v4i*>(rb + i * kRound + 16 * ln) : v4i{0, 0, 0, 0};
-          uint32_t w[8];
-          if (pow2) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t c = (uint32_t)codes[j];
-              w[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false));
-              w[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, true));
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t c = (uint32_t)codes[j];
-              const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
-              const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
-              w[2 * j] = pack_bf16(lo[0] * scale, lo[1] * scale);
-              w[2 * j + 1] = pack_bf16(hi[0] * scale, hi[1] * scale);
-            }
-          }
-          *reinterpret_cast<v4i*>(dst + 2 * (32 * pp + 16 * i)) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-          *reinterpret_cast<v4i*>(dst + 2 * (32 * pp + 16 * i + 8)) =
-              v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-        }
-        if (pp >= 1 && pp <= 8)
-          *reinterpret_cast<v4i*>(dst + 2 * (kDimV + 8 * (pp - 1))) =
-              tok_valid ? *reinterpret_cast<const v4i*>(rb + 2 * kRound + 16 * ln) : v4i{0, 0, 0, 0};
-      }
-    }
-    // block n+2 into the buffer block n-1 used (this wave's reads of it are done)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stage_block(n + 2);
-    lds_barrier();  // K tile ready
+    const uint8_t* kt = k_lds + (n & 1) * kKTile;
 
-    // ---- B: S^T = K . Q^T for heads 16w..16w+15 --------------------------------
-    // block c, accumulator row m -> token 8*(m/4) + 4c + m%4; lane (G, c16) then
-    // holds tokens 8G .. 8G+7 of head c16 in sacc[0][0..3], sacc[1][0..3].
+    // ---- S^T = K . Q^T for heads 16w..16w+15 ------------------------------------
+    // accumulator row m of the first product is K tile row m (tokens 8(m/4) + m%4),
+    // of the second row 16 + m (those + 4); lane (G, c16) then holds tokens
+    // 8G .. 8G+7 of head c16 in sacc[0][0..3], sacc[1][0..3].
     v4f sacc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
     {
-      const int tok0 = 8 * (lc16 >> 2) + (lc16 & 3);
-      const uint8_t* a0 = k_lds + tok0 * kKStride + 2 * 8 * lG;
-      const uint8_t* a1 = a0 + 4 * kKStride;
+      // operands read kAhead k-steps before their products
+      constexpr int kAhead = 2;
+      const uint8_t* a0 = kt + lc16 * kKStride + 16 * lG;
+      const uint8_t* a1 = a0 + 16 * kKStride;
+      v4i ka[kAhead], kb[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) {
+        ka[i] = *reinterpret_cast<const v4i*>(a0 + 64 * i);
+        kb[i] = *reinterpret_cast<const v4i*>(a1 + 64 * i);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);  // the first kAhead steps' reads
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const v4i ka = *reinterpret_cast<const v4i*>(a0 + 64 * ks);
-        const v4i kb = *reinterpret_cast<const v4i*>(a1 + 64 * ks);
-        sacc[0] = mfma_bf16(ka, qreg[ks], sacc[0]);
-        sacc[1] = mfma_bf16(kb, qreg[ks], sacc[1]);
+        const v4i xa = ka[ks % kAhead];
+        const v4i xb = kb[ks % kAhead];
+        if (ks + kAhead < 18) {
+          ka[ks % kAhead] = *reinterpret_cast<const v4i*>(a0 + 64 * (ks + kAhead));
+          kb[ks % kAhead] = *reinterpret_cast<const v4i*>(a1 + 64 * (ks + kAhead));
+        }
+        sacc[0] = mfma_bf16(xa, qreg[ks], sacc[0]);
+        sacc[1] = mfma_bf16(xb, qreg[ks], sacc[1]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // the two products of step ks
+        if (ks + kAhead < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of step ks + kAhead
       }
     }
     // online softmax for head c16 over tokens 8G..8G+7
     {
-      // rows of tokens 8G..8G+7 (-1: the entry selects nothing)
-      const v4i rv0 = *reinterpret_cast<const v4i*>(rows_lds + n * kBlock + 8 * lG);
-      const v4i rv1 = *reinterpret_cast<const v4i*>(rows_lds + n * kBlock + 8 * lG + 4);
+      const int32_t* ring = rows_lds + (n % kRowRing) * kBlock;
+      const v4i rv0 = *reinterpret_cast<const v4i*>(ring + 8 * lG);
+      const v4i rv1 = *reinterpret_cast<const v4i*>(ring + 8 * lG + 4);
+      const int pos0 = n * kBlock + 8 * lG;
       float x[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        x[r] = rv0[r] >= 0 ? sacc[0][r] * p.score_scale : -INFINITY;
-        x[4 + r] = rv1[r] >= 0 ? sacc[1][r] * p.score_scale : -INFINITY;
+        x[r] = valid(pos0 + r, rv0[r]) ? sacc[0][r] * p.score_scale : -INFINITY;
+        x[4 + r] = valid(pos0 + 4 + r, rv1[r]) ? sacc[1][r] * p.score_scale : -INFINITY;
       }
       float bmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       bmax = max_over_groups(bmax);
-      const float m_new = fmaxf(m_run, bmax);
+      // lazy reference: moved only when the block's maximum passes it by more
+      // than kLazyRescale (always on the first valid block, where O is still 0)
+      const bool move = bmax > m_run + kLazyRescale;
+      const float m_new = move ? bmax : m_run;
       const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_safe);  // 0 while nothing was seen
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_safe) : 1.0f;  // 0 while nothing was seen
       float e[8];
       float sum = 0.0f;
 #pragma unroll
@@ -351,19 +412,20 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         e[i] = __builtin_amdgcn_exp2f(x[i] - m_safe);
         sum += e[i];
       }
+      const bool had = m_run != -INFINITY;
       l_run = l_run * alpha + sum;
       m_run = m_new;
       const v4i pk = v4i{(int)pack_bf16(e[0], e[1]), (int)pack_bf16(e[2], e[3]), (int)pack_bf16(e[4], e[5]),
                          (int)pack_bf16(e[6], e[7])};
-      *reinterpret_cast<v4i*>(p_lds + (wave * 16 + lc16) * kBlock + 8 * lG) = pk;
+      *reinterpret_cast<v4i*>(p_lds + (lG * kHeads + wave * 16 + lc16) * 16) = pk;
       if (lG == 0) alpha_lds[wave * 16 + lc16] = alpha;
-      if (lG == 0 && alpha != 1.0f) rescale_lds = 1;  // some head's maximum moved
+      if (lG == 0 && move && had) rescale_lds[n & 1] = 1;  // accumulated O must follow the new reference
     }
-    lds_barrier();  // P and rescale factors ready
+    lds_barrier();  // P, the rescale factors and the flag are ready
 
-    // ---- C: O^T += V^T . P^T for this wave's dims, all heads ---------------------
+    // ---- O^T += V^T . P^T for this wave's dims, all heads ---------------------
     {
-      if (rescale_lds) {  // uniform: skipped once no head's maximum moves any more
+      if (rescale_lds[n & 1]) {  // uniform; rare once the references have settled
 #pragma unroll
         for (int hb = 0; hb < NW; ++hb) {
           const float al = alpha_lds[16 * hb + lc16];
@@ -371,21 +433,21 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
           for (int db = 0; db < kDB; ++db) oacc[db][hb] *= al;
         }
       }
-      // transposing reads: source lane (G, j) addresses token 8G + j/4 (+4),
-      // dims d0 + 4*(j%4); result lane (G, i) then holds dim d0 + i of tokens
-      // 8G .. 8G+7
-      const uint8_t* vbase = k_lds + (8 * lG + (lc16 >> 2)) * kKStride + 2 * (kDW * wave + 4 * (lc16 & 3));
+      // transposing reads: source lane (G, j) addresses token 8G + j/4 (K tile
+      // row 4G + j/4) and that token + 4 (row 16 + 4G + j/4), dims d0 + 4*(j%4);
+      // result lane (G, i) then holds dim d0 + i of tokens 8G .. 8G+7
+      const uint8_t* vbase = kt + (4 * lG + (lc16 >> 2)) * kKStride + 2 * (kDW * wave + 4 * (lc16 & 3));
       constexpr int kHChunk = NW < 4 ? NW : 4;  // head blocks whose P operands are held at once
 #pragma unroll
       for (int h0b = 0; h0b < NW; h0b += kHChunk) {
         v4i pb[kHChunk];
 #pragma unroll
         for (int j = 0; j < kHChunk; ++j)
-          pb[j] = *reinterpret_cast<const v4i*>(p_lds + (16 * (h0b + j) + lc16) * kBlock + 8 * lG);
+          pb[j] = *reinterpret_cast<const v4i*>(p_lds + (lG * kHeads + 16 * (h0b + j) + lc16) * 16);
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 2 * 16 * db));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 4 * kKStride + 2 * 16 * db));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 16 * kKStride + 2 * 16 * db));
           const v2i l2 = __builtin_bit_cast(v2i, lo);
           const v2i h2 = __builtin_bit_cast(v2i, hi);
           const v4i va = v4i{l2[0], l2[1], h2[0], h2[1]};
@@ -394,6 +456,9 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         }
       }
     }
+    // ---- dequantise block n+1 into the other K tile (last read in the previous step)
+    if (n + 1 < nblocks) dequant(n + 1, ln);
+    lds_barrier();  // K tile n+1 complete; P, rescale factors and K tile n no longer read
   }
 
   // ---- epilogue ----------------------------------------------------------------
@@ -513,7 +578,7 @@ int validate(const void* q, const void* kv_cache, const int32_t* indices, const 
   if (num_splits < 1 || num_splits > kMaxSplits) return BSA_ERR_SIZE;
   const int nblocks_all = (d.topk + kBlock - 1) / kBlock;
   const int bps = (nblocks_all + num_splits - 1) / num_splits;
-  if ((int64_t)bps * kBlock > kMaxTopk) return BSA_ERR_TOO_LARGE;  // a part's row list must fit in LDS
+  if ((int64_t)bps * kBlock > kMaxTopk) return BSA_ERR_TOO_LARGE;  // a part longer than the interface allows
   if (d.page_size <= 0) return BSA_ERR_PAGE_SIZE;
   if (!bsa::finite_float(d.softmax_scale)) return BSA_ERR_SOFTMAX_SCALE;
   const int nw = d.num_heads_q % 128 == 0 ? 8 : 4;  // 16 heads per wave
