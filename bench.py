@@ -75,6 +75,30 @@ def recorded_traffic(workload, op="prefill"):
     return None if rec is None else rec["hbm_bytes_per_launch"]
 
 
+WARMUP_MIN_S = 0.1   # default warm-up: at least this long (the clock settles within ~30 ms of work)
+
+
+def warm_up(step, args):
+    """Untimed warm-up: exactly --warmup steps when given, else at least 10
+    steps and at least WARMUP_MIN_S of wall time.  Returns the step count,
+    which the JSON line reports as "warmup"."""
+    import torch
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return args.warmup
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARMUP_MIN_S:
+            return n
+
+
 def qk_ceiling_tflops(qk):
     """Matrix-core ceiling of one tile's instruction mix: Q.K^T and P.V carry
     equal FLOP; with Q.K^T on f16 MFMA (half the FP8 rate) the mix tops out at
@@ -270,9 +294,7 @@ def bench_quantize_append(p, args):
                                     kscale_cache=kcache_scale, kv_layout=p.kv_layout,
                                     q_out=q_out, qscale_out=qs_out)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup = warm_up(step, args)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -292,7 +314,7 @@ def bench_quantize_append(p, args):
         "metric": "FP8 quantise-and-append HBM GB/s (algorithmic bytes)",
         "value": round(nbytes / (wall / args.steps) / 1e9, 1),
         "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 in, fp8_e4m3 out (fp32 arithmetic)",
@@ -375,9 +397,7 @@ def bench_decode(args):
             bsa.bsa_fp8_sparse_decode_ex(d["q"], d["kv_cache"], d["indices"], num_splits=splits, workspace=ws,
                                          softmax_scale=p.softmax_scale, out=out, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup = warm_up(step, args)
     if args.graph:
         # the call captured once and replayed: what a serving loop does to drop launch costs
         graph = torch.cuda.CUDAGraph()
@@ -405,11 +425,12 @@ def bench_decode(args):
     wall = time.perf_counter() - t0
     kernel_ms = np.array([s_.elapsed_time(e_) for s_, e_ in ev])
     med = float(np.median(kernel_ms)) / 1e3
+    avg = float(kernel_ms.mean()) / 1e3
     res = {
         "metric": "FP8 sparse decode TFLOPS (selected tokens, 2*(576+512) FLOP per token and head)",
         "value": round(flop / (wall / args.steps) / 1e12, 2),
         "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 (fp8_e4m3 cache dequantised to bf16, fp32 accumulate)",
@@ -418,10 +439,13 @@ def bench_decode(args):
                    "query_tokens": B * s_q, "num_splits": splits, "graph": bool(args.graph)},
         "kernel_ms_min": round(float(kernel_ms.min()), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
+        "kernel_ms_mean": round(avg * 1e3, 4),
         "kv_gbps_logical": round(nbytes / med / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(flop / med / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(flop / med / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+        # achieved over the mean launch; traffic: the rocprofv3 record of this
+        # decode source for the single-part launch of this workload, else null
+        "roofline": {"bound": "mfma", "achieved": round(flop / avg / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flop / avg / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(p.cfg.name, "decode") if splits == 1 else None},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(p, args.cpu_budget)
@@ -459,7 +483,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 10 and at least 0.1 s of them)")
     ap.add_argument("--workload", default="sparse16k")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -571,9 +596,7 @@ def main():
                                softmax_scale=p.softmax_scale, sparse_indices=si,
                                sparse_seq_len=sl, schedule=sched, qk_precision=qk, out=out, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup = warm_up(step, args)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -630,7 +653,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",

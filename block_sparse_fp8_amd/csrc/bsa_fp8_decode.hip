@@ -121,14 +121,20 @@ __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
 // is waited for explicitly.  M0 is set here and used by nothing else in this
 // kernel.
 __device__ __forceinline__ void dma_lds16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
+  // (the address is wave-uniform; readfirstlane keeps it in a scalar register
+  // even where the compiler computed it with vector instructions)
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
 }
 // Workgroup barrier that waits for this wave's LDS operations only.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Direct-to-LDS load of 4 bytes per active lane (lane l writes lds_addr + 4l).
 __device__ __forceinline__ void dma_lds4(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
 }
 
 // Staging of one block: for each group of 4 tokens ("set") a wave issues three
@@ -343,10 +349,11 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-    // Lane-derived offsets are recomputed every block from an opaque copy of the
-    // lane id rather than held in registers across the loop.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    // Lane-derived offsets are recomputed every block from a lane id made
+    // afresh (an opaque instruction, not a copy of `lane`), so that none of
+    // them is held, in registers or spilled, across the loop.
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     load_rows(n + 5, ln);   // ring slot of block n-1, last read in the previous step
     stage_block(n + 3, ln);  // staging buffer of block n, dequantised in the previous step
     if (tid == 0) rescale_lds[(n + 1) & 1] = 0;  // the next step's flag (last read in the previous step)
