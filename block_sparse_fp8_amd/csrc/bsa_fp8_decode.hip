@@ -444,7 +444,17 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
       // row 4G + j/4) and that token + 4 (row 16 + 4G + j/4), dims d0 + 4*(j%4);
       // result lane (G, i) then holds dim d0 + i of tokens 8G .. 8G+7
       const uint8_t* vbase = kt + (4 * lG + (lc16 >> 2)) * kKStride + 2 * (kDW * wave + 4 * (lc16 & 3));
-      constexpr int kHChunk = NW < 4 ? NW : 4;  // head blocks whose P operands are held at once
+      constexpr int kHChunk = 2;  // head blocks whose P operands are held at once
+      // the wave's V operands are read once and held for every head chunk
+      v4i va[kDB];
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 2 * 16 * db));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 16 * kKStride + 2 * 16 * db));
+        const v2i l2 = __builtin_bit_cast(v2i, lo);
+        const v2i h2 = __builtin_bit_cast(v2i, hi);
+        va[db] = v4i{l2[0], l2[1], h2[0], h2[1]};
+      }
 #pragma unroll
       for (int h0b = 0; h0b < NW; h0b += kHChunk) {
         v4i pb[kHChunk];
@@ -452,15 +462,9 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         for (int j = 0; j < kHChunk; ++j)
           pb[j] = *reinterpret_cast<const v4i*>(p_lds + (lG * kHeads + 16 * (h0b + j) + lc16) * 16);
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 2 * 16 * db));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 16 * kKStride + 2 * 16 * db));
-          const v2i l2 = __builtin_bit_cast(v2i, lo);
-          const v2i h2 = __builtin_bit_cast(v2i, hi);
-          const v4i va = v4i{l2[0], l2[1], h2[0], h2[1]};
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
-          for (int j = 0; j < kHChunk; ++j) oacc[db][h0b + j] = mfma_bf16(va, pb[j], oacc[db][h0b + j]);
-        }
+          for (int j = 0; j < kHChunk; ++j) oacc[db][h0b + j] = mfma_bf16(va[db], pb[j], oacc[db][h0b + j]);
       }
     }
     // ---- dequantise block n+1 into the other K tile (last read in the previous step)
