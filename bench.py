@@ -99,17 +99,33 @@ def warm_up(step, args):
             return n
 
 
+# the library's Q.K^T path when the call leaves qk_precision at its default
+DEFAULT_QK = "fp8split"
+QK_CODES = {"default": 0, "f16": 1, "fp8": 2, "fp8split": 3}
+QK_DTYPES = {
+    "f16": "Q.K^T on f16 MFMA (E4M3 codes widened exactly to f16), P.V on fp8_e4m3 MFMA, "
+           "fp32 accumulate, bf16 out",
+    "fp8": "fp8_e4m3 MFMA for Q.K^T and P.V, fp32 accumulate, bf16 out",
+    "fp8split": "fp8_e4m3 MFMA for Q.K^T (two products per K operand, query codes split by "
+                "magnitude) and P.V, fp32 accumulate, bf16 out",
+}
+
+
+def qk_path(qk):
+    return DEFAULT_QK if qk == "default" else qk
+
+
 def qk_ceiling_tflops(qk):
     """Matrix-core ceiling of one tile's instruction mix: Q.K^T and P.V carry
-    equal FLOP; with Q.K^T on f16 MFMA (half the FP8 rate) the mix tops out at
-    1 / (0.5 / 2500 + 0.5 / 5000) = 3333 TFLOP/s."""
-    if qk == "fp8":
+    equal FLOP; with Q.K^T at half the FP8 rate (f16 MFMA, or two FP8 products
+    per operand) the mix tops out at 1 / (0.5 / 2500 + 0.5 / 5000) = 3333 TFLOP/s."""
+    if qk_path(qk) == "fp8":
         return PEAK_FP8_TFLOPS
     return 1.0 / (0.5 / PEAK_F16_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
 
 
 def _clock_key(workload, qk):
-    return f"clock:{workload}:{'f16' if qk == 'default' else qk}"
+    return f"clock:{workload}:{qk_path(qk)}"
 
 
 def clock_record(workload, qk):
@@ -504,7 +520,7 @@ def main():
     ap.add_argument("--splits", default="auto",
                     help="decode only: parts per index list (an integer, or 'auto' for the library's "
                          "choice; 1 is the single-pass kernel)")
-    ap.add_argument("--qk", choices=("default", "f16", "fp8"), default="default",
+    ap.add_argument("--qk", choices=tuple(QK_CODES), default="default",
                     help="matrix path of the prefill's Q.K^T products (bsa_qk_precision)")
     ap.add_argument("--schedule", action="store_true",
                     help="run the scheduling pre-pass inside every step and launch the prefill "
@@ -577,7 +593,7 @@ def main():
                              max_seqlen_q=p.max_seqlen_q, causal=p.causal, sparse_indices=si,
                              sparse_seq_len=sl, workspace=ws, schedule=sched)
 
-    qk = {"default": 0, "f16": 1, "fp8": 2}[args.qk]
+    qk = QK_CODES[args.qk]
 
     def step():
         if args.form == "mask" and not args.schedule and qk == 0:
@@ -634,8 +650,8 @@ def main():
         flushed_ms = round(float(np.median([s.elapsed_time(e) for s, e in fe])), 4)
         del flush
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
-    # the traffic record is taken on the default launch (mask form, f16 Q.K^T)
-    recorded = args.form == "mask" and not args.schedule and args.qk != "fp8"
+    # the traffic record is taken on the default launch (mask form, default Q.K^T path)
+    recorded = args.form == "mask" and not args.schedule and qk_path(args.qk) == DEFAULT_QK
     rec = traffic_record(p.cfg.name) if recorded else None
     dram_read_gbps = None
     if rec is not None:
@@ -658,9 +674,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8_e4m3 MFMA for Q.K^T and P.V, fp32 accumulate, bf16 out" if args.qk == "fp8" else
-                  "Q.K^T on f16 MFMA (E4M3 codes widened exactly to f16), P.V on fp8_e4m3 MFMA, "
-                  "fp32 accumulate, bf16 out"),
+        "dtype": QK_DTYPES[qk_path(args.qk)],
         "data": "synthetic (seeded N(0,1) quantised to E4M3, random paging and block mask)",
         "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "active_tiles": n_act,
                    "q_tokens": T, "causal": bool(p.causal), "sparsity_form": args.form,

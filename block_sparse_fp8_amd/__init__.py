@@ -66,7 +66,8 @@ class QKPrecision(enum.IntEnum):
     """Matrix path of the prefill's Q.K^T products (bsa_qk_precision)."""
     DEFAULT = 0  # the library's choice
     F16 = 1      # E4M3 widened exactly to f16, f16 matrix products
-    FP8 = 2      # E4M3 operands on the FP8 matrix products
+    FP8 = 2      # E4M3 operands, one FP8 matrix product per K operand
+    FP8_SPLIT = 3  # E4M3 operands, two FP8 products per K operand (magnitude-split Q)
 
 
 class ScaleMode(enum.IntEnum):

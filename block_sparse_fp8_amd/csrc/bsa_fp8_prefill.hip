@@ -17,14 +17,20 @@
 //   2. Per active tile, K, V and the per-token K descales go from the paged
 //      cache straight to LDS (direct-to-LDS loads; a wave's 32 rows lie in one
 //      page, so a whole tile needs one wave-uniform page base per wave).
-//   3. S^T = K.Q^T.  By default on v_mfma_f32_32x32x16_f16: E4M3 -> f16 is
-//      exact (every E4M3 value, subnormals included, is an f16 normal), K is
-//      widened once per workgroup into an f16 tile and Q once in registers,
-//      and the product accumulates like fp32.  Optionally on the E4M3 matrix
-//      path (v_mfma_f32_32x32x64_f8f6f4), which keeps fewer bits below the
-//      largest product of a dot product.  K rows are read in a permuted order
-//      so that the accumulator registers of lane half h hold keys h*32.. of
-//      each 64-key half of the tile, in register order, the P operand's layout.
+//   3. S^T = K.Q^T on the E4M3 matrix path (v_mfma_f32_32x32x64_f8f6f4), by
+//      default with two products per K operand.  These products sum 8
+//      consecutive k at a time, each term aligned to the largest exponent sum
+//      of the eight and cut below 2^-13 of it; so each query's codes are split
+//      once between two operands, the codes within two binades of its largest
+//      magnitude and the rest, which keeps small terms out of a group with a
+//      large one (split_q).  Optionally one FP8 product per K operand (half
+//      the matrix cycles, more bits lost), or f16 products
+//      (v_mfma_f32_32x32x16_f16) on operands widened exactly (every E4M3
+//      value, subnormals included, is an f16 normal): K once per workgroup
+//      into an f16 tile, Q once in registers; they accumulate like fp32.  K
+//      rows are read in a permuted order so that the accumulator registers of
+//      lane half h hold keys h*32.. of each 64-key half of the tile, in
+//      register order, the P operand's layout.
 //   4. Online softmax in fp32 in the log2 domain: qscale*softmax_scale*log2(e)
 //      (and the per-tensor K descale) is one per-lane constant; per-token K
 //      descales multiply the scores.  P' = exp2(x - m + log2(p_scale)) =
@@ -223,6 +229,46 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
+// Matrix paths of the Q.K^T products (template argument of the kernel).
+constexpr int kQkF16 = 0;       // E4M3 widened exactly to f16, f16 products
+constexpr int kQkFp8 = 1;       // E4M3 operands, one FP8 product per K operand
+constexpr int kQkFp8Split = 2;  // E4M3 operands, two FP8 products per K operand
+
+// Magnitude split of a query's E4M3 codes between two FP8 products.
+// The FP8 products sum 8 consecutive k at a time, each term aligned to the
+// largest exponent sum of the eight and cut below 2^-13 of it, so small terms
+// beside a large one lose bits.  Codes within two binades of the query's
+// largest magnitude (magnitude code >= max - 16) stay in `a`; the others move
+// to `b`, and each position holds its code in exactly one of the two (+0 in
+// the other), so the two products sum to the same dot product.  A lane holds
+// half of its query's dims and lane l ^ 32 the other half, so the maximum is
+// taken over both.  E4M3 magnitudes order like their 7-bit codes, so the test
+// is a byte compare.
+__device__ __forceinline__ void split_q(v8i* a, v8i* b) {
+  uint32_t mx = 0;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t m = (uint32_t)a[ks][i] & 0x7f7f7f7fu;
+      mx = max(mx, max(max(m & 0xffu, (m >> 8) & 0xffu), max((m >> 16) & 0xffu, m >> 24)));
+    }
+  const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+  mx = max(sw[0], sw[1]);
+  const uint32_t thr = mx > 16u ? mx - 16u : 0u;
+  const uint32_t add = (0x80u - thr) * 0x01010101u;  // bit 7 of a byte set iff its magnitude >= thr
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = (uint32_t)a[ks][i];
+      const uint32_t sel = ((w & 0x7f7f7f7fu) + add) & 0x80808080u;
+      const uint32_t keep = sel | (sel - (sel >> 7));  // 0xff where selected
+      a[ks][i] = (int)(w & keep);
+      b[ks][i] = (int)(w & ~keep);
+    }
+}
+
 // The software-pipelined tile loop.  Per active tile t (with t1, t2 the next
 // two) each wave runs two phases whose matrix products and VALU work are
 // independent, so that one wave keeps both the matrix pipe and the VALU busy:
@@ -236,9 +282,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Loads of a step (V(t), the K descales of t1, the raw K of t2, the page ids
 // of the tile after t2) are issued at its start and waited for before the
 // barrier that separates A from B.
-template <int QUANT, int FORM, bool QK8>
+template <int QUANT, int FORM, int QKM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bsa_fp8_prefill_kernel(Params p) {
+  constexpr bool QK8 = QKM != kQkF16;          // E4M3 operands on the FP8 products
+  constexpr bool SPLIT = QKM == kQkFp8Split;   // two products per K operand (split Q)
   // K for the products: f16 chunk-major tile (32 KB: 16-byte chunk c, dims
   // 8c..8c+7, of key row r at c*2048 + r*16) fed from an E4M3 staging tile; or
   // (FP8 products) a ring of two E4M3 tiles.  E4M3 tiles are row-major with
@@ -332,6 +380,7 @@ bsa_fp8_prefill_kernel(Params p) {
   // ks*64 + hd*32 .. +31 for ks = 0..1.
   v8h qh[QK8 ? 1 : 8];
   v8i q8[QK8 ? 2 : 1];
+  v8i q8b[SPLIT ? 2 : 1];  // split products: the codes of the second product
   v2i qraw[QK8 ? 1 : 8];
   float cscale = 0.0f;
   {
@@ -348,6 +397,7 @@ bsa_fp8_prefill_kernel(Params p) {
     }
     if (q_valid) cscale = p.qscale[qi] * p.qk_scale;
   }
+  if constexpr (SPLIT) split_q(q8, q8b);
   auto widen_q = [&]() {
     if constexpr (!QK8) {
 #pragma unroll
@@ -494,7 +544,8 @@ bsa_fp8_prefill_kernel(Params p) {
     }
   };
   auto mfma_qk = [&](const KOp& a, int ks, const v16f& acc) -> v16f {
-    if constexpr (QK8) return mfma_f8(a, q8[ks], acc);
+    if constexpr (SPLIT) return mfma_f8(a, q8b[ks], mfma_f8(a, q8[ks], acc));
+    else if constexpr (QK8) return mfma_f8(a, q8[ks], acc);
     else return mfma_f16(a, qh[ks], acc);
   };
   // All four blocks of a tile with no other work (the prologue).
@@ -718,9 +769,17 @@ bsa_fp8_prefill_kernel(Params p) {
       // interleave: each product with its operand read and a share of the softmax
 #pragma unroll
       for (int ks = 0; ks < kPerBlock; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, QK8 ? 2 : 1, 0);      // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, QK8 ? 24 : 6, 0);     // VALU
+        if constexpr (SPLIT) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0); // VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0); // VALU
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, QK8 ? 2 : 1, 0);      // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, QK8 ? 24 : 6, 0);     // VALU
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -876,13 +935,14 @@ int bsa_fp8_prefill_ex(const void* q, const void* kcache, const void* vcache, co
   const bool q1 = quant_type == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD;
   constexpr int Q0 = BSA_QUANT_Q_TOKHEAD_K_TENSOR_V_TENSOR, Q1 = BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD;
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid3, block3, 0, s, p); };
-  if (r.qk8) {
-    if (q1) list ? go(bsa_fp8_prefill_kernel<Q1, kFormList, true>) : go(bsa_fp8_prefill_kernel<Q1, 0, true>);
-    else list ? go(bsa_fp8_prefill_kernel<Q0, kFormList, true>) : go(bsa_fp8_prefill_kernel<Q0, 0, true>);
-  } else {
-    if (q1) list ? go(bsa_fp8_prefill_kernel<Q1, kFormList, false>) : go(bsa_fp8_prefill_kernel<Q1, 0, false>);
-    else list ? go(bsa_fp8_prefill_kernel<Q0, kFormList, false>) : go(bsa_fp8_prefill_kernel<Q0, 0, false>);
-  }
+  auto pick = [&](auto qkm) {
+    constexpr int M = decltype(qkm)::value;
+    if (q1) list ? go(bsa_fp8_prefill_kernel<Q1, kFormList, M>) : go(bsa_fp8_prefill_kernel<Q1, 0, M>);
+    else list ? go(bsa_fp8_prefill_kernel<Q0, kFormList, M>) : go(bsa_fp8_prefill_kernel<Q0, 0, M>);
+  };
+  if (r.qk == BSA_QK_FP8) pick(std::integral_constant<int, kQkFp8>{});
+  else if (r.qk == BSA_QK_FP8_SPLIT) pick(std::integral_constant<int, kQkFp8Split>{});
+  else pick(std::integral_constant<int, kQkF16>{});
   if (hipGetLastError() != hipSuccess) return BSA_ERR_LAUNCH;
   return BSA_OK;
 }

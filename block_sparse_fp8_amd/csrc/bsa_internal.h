@@ -45,7 +45,7 @@ struct Resolved {
   int q_layout;
   float p_scale;
   const int32_t* schedule;
-  bool qk8;          // Q.K^T on the FP8 matrix path
+  int qk;            // Q.K^T matrix path: BSA_QK_F16, BSA_QK_FP8 or BSA_QK_FP8_SPLIT
 };
 
 inline bool finite_float(float x) {
@@ -95,7 +95,8 @@ inline int resolve(const bsa_fp8_dims* dims, const uint8_t* block_mask, const bs
   const int64_t tasks = (int64_t)d.batch * d.num_heads_q * mt_grid;
   if (tasks > 0x7fffffffLL) return BSA_ERR_TOO_LARGE;
   if (o.schedule != nullptr && o.schedule_len != tasks) return BSA_ERR_SCHEDULE;
-  if (o.qk_precision != BSA_QK_DEFAULT && o.qk_precision != BSA_QK_F16 && o.qk_precision != BSA_QK_FP8)
+  if (o.qk_precision != BSA_QK_DEFAULT && o.qk_precision != BSA_QK_F16 && o.qk_precision != BSA_QK_FP8 &&
+      o.qk_precision != BSA_QK_FP8_SPLIT)
     return BSA_ERR_QK_PRECISION;
 
   r->d = d;
@@ -108,7 +109,7 @@ inline int resolve(const bsa_fp8_dims* dims, const uint8_t* block_mask, const bs
   r->q_layout = o.q_layout;
   r->p_scale = ps;
   r->schedule = o.schedule;
-  r->qk8 = o.qk_precision == BSA_QK_FP8;
+  r->qk = o.qk_precision == BSA_QK_DEFAULT ? BSA_QK_FP8_SPLIT : o.qk_precision;
   return BSA_OK;
 }
 

@@ -38,7 +38,7 @@ def test_committed_records_are_well_formed():
         if key.startswith("clock:"):
             # shader clock of the prefill: plausible for an MI355X (at most 2.4 GHz)
             _, wl, qk = key.split(":")
-            assert qk in ("f16", "fp8"), key
+            assert qk in ("f16", "fp8", "fp8split"), key
             assert 0.5 < rec["clock_ghz_min"] <= rec["clock_ghz_mean"] <= rec["clock_ghz_max"] <= 2.5, key
             assert rec["num_xcc"] == 8 and rec["dispatches"] > 0, key
             continue
@@ -50,11 +50,11 @@ def test_committed_records_are_well_formed():
 def test_clock_record_is_per_path_and_source(tmp_path, monkeypatch):
     path = tmp_path / "traffic.json"
     good = {"kernel_source_sha256": bench.kernel_source_hash("prefill"), "clock_ghz_mean": 1.9}
-    recs = {"clock:wl:f16": good, "clock:wl:fp8": dict(good, kernel_source_sha256="0" * 64)}
+    recs = {f"clock:wl:{bench.DEFAULT_QK}": good, "clock:wl:fp8": dict(good, kernel_source_sha256="0" * 64)}
     path.write_text(json.dumps(recs))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
-    assert bench.clock_record("wl", "default")["clock_ghz_mean"] == 1.9   # default = f16 products
-    assert bench.clock_record("wl", "f16")["clock_ghz_mean"] == 1.9
+    assert bench.clock_record("wl", "default")["clock_ghz_mean"] == 1.9   # the library's default path
+    assert bench.clock_record("wl", bench.DEFAULT_QK)["clock_ghz_mean"] == 1.9
     assert bench.clock_record("wl", "fp8") is None                       # taken for another source
     assert bench.clock_record("other", "default") is None
 
@@ -64,3 +64,5 @@ def test_mix_ceiling():
     assert abs(bench.qk_ceiling_tflops("default") - 10000.0 / 3.0) < 1e-6
     assert abs(bench.qk_ceiling_tflops("f16") - 10000.0 / 3.0) < 1e-6
     assert bench.qk_ceiling_tflops("fp8") == 5000.0
+    # two FP8 products per K operand: Q.K^T at half the FP8 rate, like f16
+    assert abs(bench.qk_ceiling_tflops("fp8split") - 10000.0 / 3.0) < 1e-6
