@@ -113,8 +113,11 @@ struct Params {
   int head_stride;      // rows between consecutive kv-heads of a page (1 for NHD, page_size for HND)
 };
 
-// 16-byte chunk swizzle of the fp8 V rows (128 B, 8 chunks) in LDS.
-__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ (((row >> 5) & 1) << 2); }
+// 16-byte chunk swizzle of the E4M3 K and V rows (128 B, 8 chunks) in LDS:
+// chunk c of row r sits at c ^ (r & 7) ^ bit 5 of r.  Both read patterns are
+// then free of bank conflicts: the transposing V reads, and the FP8 K operand
+// reads, whose 16 lanes per pass take rows r0+{0..3, 4..7, 32..35, 36..39}.
+__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 5) & 1); }
 
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -642,7 +645,7 @@ bsa_fp8_prefill_kernel(Params p) {
     const int grp = ln >> 4;
     const int kk = (ln & 15) >> 1;
     const int half = grp >> 1;
-    const int csw = (grp & 1) ^ kk ^ (half << 2);  // logical chunk 2d + (grp&1), swizzled
+    const int csw = (grp & 1) ^ kk ^ half;  // logical chunk 2d + (grp&1), swizzled
     const uint8_t* vp = v8_lds + (half * 32 + kk) * kHeadDim + 8 * (ln & 1) + (((2 * (x & 3)) ^ csw) << 4) +
                         (x >> 2) * 64 * kHeadDim;
     v8i a;
