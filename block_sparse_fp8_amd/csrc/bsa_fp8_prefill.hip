@@ -297,8 +297,11 @@ bsa_fp8_prefill_kernel(Params p) {
   constexpr int kKBytes = QK8 ? 2 * kTile * kHeadDim : kTile * kK16Row;
   __shared__ __attribute__((aligned(16))) uint8_t kmat_lds[kKBytes];
   __shared__ __attribute__((aligned(16))) uint8_t kst_lds[QK8 ? 16 : kTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint8_t v8_lds[kTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) float ks_lds[kTile];
+  // V and the K descales: on the FP8 paths two buffers each (step parity), so
+  // that a step needs one barrier; the f16 path has room for one of each.
+  constexpr int kVBufs = QK8 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t v8_lds[kVBufs * kTile * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float ks_lds[kVBufs * kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -489,13 +492,13 @@ bsa_fp8_prefill_kernel(Params p) {
   // The K descales of the wave's 32 rows (lanes 0..31, one float each) from
   // the same page: the descale array is laid out like the cache without the
   // head dimension.  Rows past the KV length read row lkv-1.
-  auto dma_kscale = [&](int n, int pg, int ln) {
+  auto dma_kscale = [&](int n, int pg, int ln, int slot) {
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
       const int row = n * kTile + wave * 32 + (ln & 31);
       const uint32_t off = (uint32_t)((min(row, lkv - 1) & pmask) * p.slot_stride + head_row) * 4u;
       const uint64_t sbase = (uint64_t)(uintptr_t)p.kscale +
                              (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(pg) * (p.page_bytes / kHeadDim) * 4u;
-      if (ln < 32) dma4s(off, sbase, lds_addr(ks_lds) + wave * 32 * 4);
+      if (ln < 32) dma4s(off, sbase, lds_addr(ks_lds + slot * kTile) + wave * 32 * 4);
     }
   };
   // f16 products: widen the staged E4M3 K tile into the f16 tile.  Thread
@@ -568,10 +571,10 @@ bsa_fp8_prefill_kernel(Params p) {
   // Scale + band mask + maximum of one block of S (in place); returns the
   // block's partial maximum of the unscaled-by-cscale score.
   // The K descales of block c (per-token K scales), read ahead of their use.
-  auto ks_read = [&](int c, int ln) -> v16f {
+  auto ks_read = [&](int c, int ln, int slot) -> v16f {
     v16f k;
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
-      const float* ksp = &ks_lds[(c >> 1) * 64 + (ln >> 5) * 32 + (c & 1) * 16];
+      const float* ksp = &ks_lds[slot * kTile + (c >> 1) * 64 + (ln >> 5) * 32 + (c & 1) * 16];
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
         const v4f t = *reinterpret_cast<const v4f*>(ksp + r);
@@ -641,12 +644,13 @@ bsa_fp8_prefill_kernel(Params p) {
   // lane i then holds column base + i for those 8 keys.  Rows sp*64 +
   // half*32 + 8*rr + kk all share this lane's chunk swizzle, so one base per
   // block serves the whole tile.
-  auto vread = [&](int x, int ln) -> v8i {  // x = sp*4 + d
+  auto vread = [&](int x, int ln, int slot) -> v8i {  // x = sp*4 + d
     const int grp = ln >> 4;
     const int kk = (ln & 15) >> 1;
     const int half = grp >> 1;
     const int csw = (grp & 1) ^ kk ^ half;  // logical chunk 2d + (grp&1), swizzled
-    const uint8_t* vp = v8_lds + (half * 32 + kk) * kHeadDim + 8 * (ln & 1) + (((2 * (x & 3)) ^ csw) << 4) +
+    const uint8_t* vp = v8_lds + slot * kTile * kHeadDim + (half * 32 + kk) * kHeadDim + 8 * (ln & 1) +
+                        (((2 * (x & 3)) ^ csw) << 4) +
                         (x >> 2) * 64 * kHeadDim;
     v8i a;
 #pragma unroll
@@ -698,7 +702,7 @@ bsa_fp8_prefill_kernel(Params p) {
   // K(n1) into the product tile.
   uint8_t* kslot0 = QK8 ? kmat_lds : kst_lds;  // where K(n) lands
   dma_tile(p.kc, n, pg_n.kv, kslot0, lane);
-  dma_kscale(n, pg_n.kv, lane);
+  dma_kscale(n, pg_n.kv, lane, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 #pragma unroll
@@ -710,7 +714,7 @@ bsa_fp8_prefill_kernel(Params p) {
     qk_tile(sa, lane, kslot0);
     float tm = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) tm = prep_block(sa[c], ks_read(c, lane), c, n, lane, tm);
+    for (int c = 0; c < 4; ++c) tm = prep_block(sa[c], ks_read(c, lane, 0), c, n, lane, tm);
     update_max(tm);
   }
   __syncthreads();  // every wave is done with K(n) and the descales of n
@@ -733,9 +737,11 @@ bsa_fp8_prefill_kernel(Params p) {
     // is waited for at once, which must not also wait for the tile loads)
     const int n3 = n2 >= 0 ? walk.next(ln) : -1;
     const Pages pg_3 = n3 >= 0 ? lookup(n3, ln) : Pages{0};
-    // loads of the step: V(n), the descales of n1, K(n2)
-    dma_tile(p.vc, n, pg_n.kv, v8_lds, ln);
-    if (n1 >= 0) dma_kscale(n1, pg_1.kv, ln);
+    // loads of the step: V(n), the descales of n1, K(n2); on the FP8 paths V
+    // and the descales alternate between two buffers by step parity
+    constexpr int vs = QK8 ? par : 0;
+    dma_tile(p.vc, n, pg_n.kv, v8_lds + vs * kTile * kHeadDim, ln);
+    if (n1 >= 0) dma_kscale(n1, pg_1.kv, ln, vs);
     uint8_t* k2dst = QK8 ? kmat_lds + (par ^ 1) * kTile * kHeadDim : kst_lds;
     if (n2 >= 0) dma_tile(p.kc, n2, pg_2.kv, k2dst, ln);
 
@@ -800,7 +806,7 @@ bsa_fp8_prefill_kernel(Params p) {
     // (the factor is exactly 1 when no row of the wave has a new maximum;
     // multiplying anyway keeps the phase free of branches)
     const float sc = rescale ? alpha : 1.0f;
-    v8i va0 = vread(0, ln), va1 = vread(4, ln);
+    v8i va0 = vread(0, ln, vs), va1 = vread(4, ln, vs);
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[0][r] *= sc;
     float tm = -INFINITY;
@@ -809,20 +815,25 @@ bsa_fp8_prefill_kernel(Params p) {
       oacc[d] = mfma_f8(va0, pk[0], oacc[d]);
       oacc[d] = mfma_f8(va1, pk[1], oacc[d]);
       {
-        const v16f kd = ks_read(d, ln);  // dead before the next block's V operands are read
+        const v16f kd = ks_read(d, ln, vs);  // dead before the next block's V operands are read
         widen_k(d, ln);
         tm = prep_block(nxt[d], kd, d, n1, ln, tm);
       }
       if (d < 3) {
-        va0 = vread(d + 1, ln);
-        va1 = vread(5 + d, ln);
+        va0 = vread(d + 1, ln, vs);
+        va1 = vread(5 + d, ln, vs);
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d + 1][r] *= sc;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (n1 >= 0) update_max(tm);
-    __syncthreads();  // V(n) and the descales no longer read; K(n2) is ready
+    // f16 path: V(n) and the descales are no longer read, and K(n2) is
+    // widened.  The FP8 paths need no barrier here: the next step writes the
+    // other V and descale buffers and the K slot that held K(n1), and no wave
+    // starts it before every wave has passed this step's barrier, i.e. is done
+    // with the products that read K(n1) and with the previous step's P.V.
+    if constexpr (!QK8) __syncthreads();
     n = n1;
     n1 = n2;
     n2 = n3;
