@@ -61,7 +61,7 @@ constexpr int kDimV = 512;
 constexpr int kRowBytes = 656;
 constexpr int kKStride = kDimK * 2 + 32;   // bytes per LDS K row (padded: conflict-free reads)
 constexpr int kMaxTopk = BSA_DECODE_MAX_TOPK;  // longest index list one workgroup walks (interface limit)
-constexpr int kStages = 3;                 // staging ring: block n+3 loads while n+1 is dequantised
+constexpr int kKTiles = 3;                 // K tiles: P.V of block n-1, Q.K^T of n, dequantisation of n+1
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegFltMax = -3.402823466e+38f;
@@ -166,14 +166,13 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   constexpr int kWaveStage = kSets * 3 * kRound;
   constexpr int kStageBytes = NW * kWaveStage;  // one block
   constexpr int kKTile = kBlock * kKStride;
-  constexpr int kLoadsPerStep = 1 + 3 * kSets;  // direct-to-LDS loads a wave issues per block
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2 * kKTile];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[kStages * kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[4 * kHeads * 16];  // [token group][head][8 tokens]
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKTiles * kKTile];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[kStageBytes];  // one block, a region per wave
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2 * 4 * kHeads * 16];  // [block parity][token group][head][8 tokens]
   __shared__ __attribute__((aligned(16))) int32_t rows_lds[kRowRing * kBlock];
-  __shared__ float alpha_lds[kHeads];
+  __shared__ float alpha_lds[2 * kHeads];  // [block parity][head]
   __shared__ float l_lds[kHeads];
-  __shared__ int rescale_lds[2];  // per step parity: some head's reference maximum moved
+  __shared__ int rescale_lds[3];  // [block % 3]: some head's reference maximum moved
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -212,6 +211,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   if (tid == 0) {
     rescale_lds[0] = 0;
     rescale_lds[1] = 0;
+    rescale_lds[2] = 0;
   }
 
   const uint32_t k_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)k_lds);
@@ -227,9 +227,10 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
     const int pos = min(k * kBlock + ln, lim - 1);
     if (ln < kBlock) dma_lds4(idx_row + pos, rows_base + (uint32_t)((k % kRowRing) * kBlock * 4));
   };
-  // Rows of block k into staging buffer k % kStages (the same number of loads
+  // Rows of block k into this wave's staging region (the same number of loads
   // for every block, so that waits can count them; an entry that names no row
-  // loads row 0, which exists whenever there is a block).
+  // loads row 0, which exists whenever there is a block).  Each wave stages and
+  // dequantises its own tokens, so its region needs no barrier between uses.
   auto stage_block = [&](int k, int ln) {
     const int32_t* ring = rows_lds + (k % kRowRing) * kBlock;
     const int pp = ln & 15;
@@ -238,13 +239,13 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
       const int t = (wave * kSets + st) * 4 + (ln >> 4);
       const int r = ring[t];
       const uint8_t* src = p.kv + (int64_t)(valid(k * kBlock + t, r) ? r : 0) * kRowBytes;
-      const uint32_t dst = stage_base + (uint32_t)((k % kStages) * kStageBytes + st * 3 * kRound);
+      const uint32_t dst = stage_base + (uint32_t)(st * 3 * kRound);
       dma_lds16(src + 16 * pp, dst);
       dma_lds16(src + 256 + 16 * pp, dst + kRound);
       dma_lds16(src + kDimV + 16 * min(pp, 8), dst + 2 * kRound);
     }
   };
-  // Dequantise block k from its staging buffer into K tile k & 1: lane (tl, p)
+  // Dequantise block k from the staging region into K tile k % 3: lane (tl, p)
   // converts codes 128j + 8p .. +7 (tile j = 0..3) of its token and writes them
   // as 16 bytes of bfloat16 at 256j + 16p of the token's row, so the 16 lanes
   // of a token write 256 consecutive bytes per instruction; lanes p = 1..8
@@ -252,8 +253,8 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   // row 0, which may hold anything: its K/V values are written as zeros, so
   // that its zero probability cannot meet a NaN or infinity in the products.
   auto dequant = [&](int k, int ln) {
-    const uint8_t* sb = stage_lds + (k % kStages) * kStageBytes + wave * kWaveStage;
-    uint8_t* kt = k_lds + (k & 1) * kKTile;
+    const uint8_t* sb = stage_lds + wave * kWaveStage;
+    uint8_t* kt = k_lds + (k % kKTiles) * kKTile;
     const int32_t* ring = rows_lds + (k % kRowRing) * kBlock;
     const int tl = ln >> 4;
     const int pp = ln & 15;
@@ -320,53 +321,47 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   float m_run = -INFINITY;  // reference maximum per head (column c16 of this wave), log2 domain
   float l_run = 0.0f;       // this lane's share of the row sum, relative to the reference
 
-  // Per step n the loads of a wave are: the row ids of block n+5, then the
-  // rows of block n+3; the staging of block k is dequantised at step k-1.
-  // In the prologue the same order is set up for blocks 0..4 / 0..2.
+  // Step n (n = 0 .. nblocks) runs, with one barrier at its end:
+  //   Q.K^T of block n (K tile n % 3) beside the dequantisation of block n+1
+  //   (into K tile (n+1) % 3, from this wave's staging region), then
+  //   P.V of block n-1 (K tile (n-1) % 3, P buffer (n-1) & 1) beside the
+  //   softmax of block n (into P buffer n & 1).
+  // Loads of a wave per step: the row ids of block n+3 at the start, the rows
+  // of block n+2 once its staging region has been read.  A K tile is rewritten
+  // two steps after its Q.K^T and one after its P.V, a P buffer one step after
+  // its P.V, so the end-of-step barrier orders every reuse.
   if (nblocks > 0) {
     load_rows(0, lane);
     load_rows(1, lane);
     load_rows(2, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     stage_block(0, lane);
-    load_rows(3, lane);
-    stage_block(1, lane);
-    load_rows(4, lane);
-    stage_block(2, lane);
-    // block 0 has arrived once only the loads of blocks 1 and 2 remain
-    if constexpr (kLoadsPerStep == 4)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     dequant(0, lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the staging region has been read
+    stage_block(1, lane);
   }
   lds_barrier();  // K tile 0 and the flags are ready
 
-  for (int n = 0; n < nblocks; ++n) {
-    // the loads issued two steps ago (row ids of n+3, rows of n+1) are complete
-    // once at most the previous step's remain in flight
-    if constexpr (kLoadsPerStep == 4)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  const int nsteps = nblocks > 0 ? nblocks + 1 : 0;
+  for (int n = 0; n < nsteps; ++n) {
     // Lane-derived offsets are recomputed every block from a lane id made
     // afresh (an opaque instruction, not a copy of `lane`), so that none of
     // them is held, in registers or spilled, across the loop.
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    load_rows(n + 5, ln);   // ring slot of block n-1, last read in the previous step
-    stage_block(n + 3, ln);  // staging buffer of block n, dequantised in the previous step
-    if (tid == 0) rescale_lds[(n + 1) & 1] = 0;  // the next step's flag (last read in the previous step)
+    load_rows(n + 3, ln);  // ring slot of block n-3, last read in step n-3
+    if (tid == 0) rescale_lds[(n + 1) % 3] = 0;  // written in step n+1; last read in step n-1
     const int lG = ln >> 4;
     const int lc16 = ln & 15;
-    const uint8_t* kt = k_lds + (n & 1) * kKTile;
 
     // ---- S^T = K . Q^T for heads 16w..16w+15 ------------------------------------
     // accumulator row m of the first product is K tile row m (tokens 8(m/4) + m%4),
     // of the second row 16 + m (those + 4); lane (G, c16) then holds tokens
     // 8G .. 8G+7 of head c16 in sacc[0][0..3], sacc[1][0..3].
     v4f sacc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
-    {
+    if (n < nblocks) {
+      const uint8_t* kt = k_lds + (n % kKTiles) * kKTile;
       // operands read kAhead k-steps before their products
       constexpr int kAhead = 2;
       const uint8_t* a0 = kt + lc16 * kKStride + 16 * lG;
@@ -392,8 +387,56 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         if (ks + kAhead < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of step ks + kAhead
       }
     }
-    // online softmax for head c16 over tokens 8G..8G+7
-    {
+    // ---- dequantise block n+1 ------------------------------------------------------
+    // the rows of block n+1 and the row ids of n+2 (issued in the previous
+    // step) are complete once only this step's row-id load is in flight
+    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    if (n + 1 < nblocks) dequant(n + 1, ln);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the staging region has been read
+    stage_block(n + 2, ln);
+
+    // ---- O^T += V^T . P^T of block n-1 for this wave's dims, all heads ---------
+    if (n >= 1) {
+      const int np = n - 1;
+      if (rescale_lds[np % 3]) {  // uniform; rare once the references have settled
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb) {
+          const float al = alpha_lds[(np & 1) * kHeads + 16 * hb + lc16];
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) oacc[db][hb] *= al;
+        }
+      }
+      const uint8_t* kt = k_lds + (np % kKTiles) * kKTile;
+      const uint8_t* pbuf = p_lds + (np & 1) * (4 * kHeads * 16);
+      // transposing reads: source lane (G, j) addresses token 8G + j/4 (K tile
+      // row 4G + j/4) and that token + 4 (row 16 + 4G + j/4), dims d0 + 4*(j%4);
+      // result lane (G, i) then holds dim d0 + i of tokens 8G .. 8G+7
+      const uint8_t* vbase = kt + (4 * lG + (lc16 >> 2)) * kKStride + 2 * (kDW * wave + 4 * (lc16 & 3));
+      constexpr int kHChunk = 2;  // head blocks whose P operands are held at once
+      // the wave's V operands are read once and held for every head chunk
+      v4i va[kDB];
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 2 * 16 * db));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 16 * kKStride + 2 * 16 * db));
+        const v2i l2 = __builtin_bit_cast(v2i, lo);
+        const v2i h2 = __builtin_bit_cast(v2i, hi);
+        va[db] = v4i{l2[0], l2[1], h2[0], h2[1]};
+      }
+#pragma unroll
+      for (int h0b = 0; h0b < NW; h0b += kHChunk) {
+        v4i pb[kHChunk];
+#pragma unroll
+        for (int j = 0; j < kHChunk; ++j)
+          pb[j] = *reinterpret_cast<const v4i*>(pbuf + (lG * kHeads + 16 * (h0b + j) + lc16) * 16);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int j = 0; j < kHChunk; ++j) oacc[db][h0b + j] = mfma_bf16(va[db], pb[j], oacc[db][h0b + j]);
+      }
+    }
+    // ---- online softmax of block n for head c16 over tokens 8G..8G+7 -------------
+    if (n < nblocks) {
       const int32_t* ring = rows_lds + (n % kRowRing) * kBlock;
       const v4i rv0 = *reinterpret_cast<const v4i*>(ring + 8 * lG);
       const v4i rv1 = *reinterpret_cast<const v4i*>(ring + 8 * lG + 4);
@@ -424,52 +467,11 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
       m_run = m_new;
       const v4i pk = v4i{(int)pack_bf16(e[0], e[1]), (int)pack_bf16(e[2], e[3]), (int)pack_bf16(e[4], e[5]),
                          (int)pack_bf16(e[6], e[7])};
-      *reinterpret_cast<v4i*>(p_lds + (lG * kHeads + wave * 16 + lc16) * 16) = pk;
-      if (lG == 0) alpha_lds[wave * 16 + lc16] = alpha;
-      if (lG == 0 && move && had) rescale_lds[n & 1] = 1;  // accumulated O must follow the new reference
+      *reinterpret_cast<v4i*>(p_lds + (n & 1) * (4 * kHeads * 16) + (lG * kHeads + wave * 16 + lc16) * 16) = pk;
+      if (lG == 0) alpha_lds[(n & 1) * kHeads + wave * 16 + lc16] = alpha;
+      if (lG == 0 && move && had) rescale_lds[n % 3] = 1;  // accumulated O must follow the new reference
     }
-    lds_barrier();  // P, the rescale factors and the flag are ready
-
-    // ---- O^T += V^T . P^T for this wave's dims, all heads ---------------------
-    {
-      if (rescale_lds[n & 1]) {  // uniform; rare once the references have settled
-#pragma unroll
-        for (int hb = 0; hb < NW; ++hb) {
-          const float al = alpha_lds[16 * hb + lc16];
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) oacc[db][hb] *= al;
-        }
-      }
-      // transposing reads: source lane (G, j) addresses token 8G + j/4 (K tile
-      // row 4G + j/4) and that token + 4 (row 16 + 4G + j/4), dims d0 + 4*(j%4);
-      // result lane (G, i) then holds dim d0 + i of tokens 8G .. 8G+7
-      const uint8_t* vbase = kt + (4 * lG + (lc16 >> 2)) * kKStride + 2 * (kDW * wave + 4 * (lc16 & 3));
-      constexpr int kHChunk = 2;  // head blocks whose P operands are held at once
-      // the wave's V operands are read once and held for every head chunk
-      v4i va[kDB];
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 2 * 16 * db));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase + 16 * kKStride + 2 * 16 * db));
-        const v2i l2 = __builtin_bit_cast(v2i, lo);
-        const v2i h2 = __builtin_bit_cast(v2i, hi);
-        va[db] = v4i{l2[0], l2[1], h2[0], h2[1]};
-      }
-#pragma unroll
-      for (int h0b = 0; h0b < NW; h0b += kHChunk) {
-        v4i pb[kHChunk];
-#pragma unroll
-        for (int j = 0; j < kHChunk; ++j)
-          pb[j] = *reinterpret_cast<const v4i*>(p_lds + (lG * kHeads + 16 * (h0b + j) + lc16) * 16);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-#pragma unroll
-          for (int j = 0; j < kHChunk; ++j) oacc[db][h0b + j] = mfma_bf16(va[db], pb[j], oacc[db][h0b + j]);
-      }
-    }
-    // ---- dequantise block n+1 into the other K tile (last read in the previous step)
-    if (n + 1 < nblocks) dequant(n + 1, ln);
-    lds_barrier();  // K tile n+1 complete; P, rescale factors and K tile n no longer read
+    lds_barrier();  // K tile n+1, P of block n, its factors and flag are ready; tile n-1 is free
   }
 
   // ---- epilogue ----------------------------------------------------------------
