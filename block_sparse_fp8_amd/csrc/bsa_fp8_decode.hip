@@ -47,6 +47,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
+#include <type_traits>
 
 #include "bsa_fp8.h"
 #include "bsa_internal.h"
@@ -343,8 +344,12 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
   }
   lds_barrier();  // K tile 0 and the flags are ready
 
-  const int nsteps = nblocks > 0 ? nblocks + 1 : 0;
-  for (int n = 0; n < nsteps; ++n) {
+  // The first step has no P.V and the last no Q.K^T or softmax; the steps
+  // between have both, as straight-line code that the scheduler can
+  // interleave.
+  auto step = [&](int n, auto qk_tag, auto pv_tag) __attribute__((always_inline)) {
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool PV = decltype(pv_tag)::value;
     // Lane-derived offsets are recomputed every block from a lane id made
     // afresh (an opaque instruction, not a copy of `lane`), so that none of
     // them is held, in registers or spilled, across the loop.
@@ -360,7 +365,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
     // of the second row 16 + m (those + 4); lane (G, c16) then holds tokens
     // 8G .. 8G+7 of head c16 in sacc[0][0..3], sacc[1][0..3].
     v4f sacc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
-    if (n < nblocks) {
+    if constexpr (QK) {
       const uint8_t* kt = k_lds + (n % kKTiles) * kKTile;
       // operands read kAhead k-steps before their products
       constexpr int kAhead = 2;
@@ -396,7 +401,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
     stage_block(n + 2, ln);
 
     // ---- O^T += V^T . P^T of block n-1 for this wave's dims, all heads ---------
-    if (n >= 1) {
+    if constexpr (PV) {
       const int np = n - 1;
       if (rescale_lds[np % 3]) {  // uniform; rare once the references have settled
 #pragma unroll
@@ -436,7 +441,7 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
       }
     }
     // ---- online softmax of block n for head c16 over tokens 8G..8G+7 -------------
-    if (n < nblocks) {
+    if constexpr (QK) {
       const int32_t* ring = rows_lds + (n % kRowRing) * kBlock;
       const v4i rv0 = *reinterpret_cast<const v4i*>(ring + 8 * lG);
       const v4i rv1 = *reinterpret_cast<const v4i*>(ring + 8 * lG + 4);
@@ -472,6 +477,11 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
       if (lG == 0 && move && had) rescale_lds[n % 3] = 1;  // accumulated O must follow the new reference
     }
     lds_barrier();  // K tile n+1, P of block n, its factors and flag are ready; tile n-1 is free
+  };
+  if (nblocks > 0) {
+    step(0, std::true_type{}, std::false_type{});
+    for (int n = 1; n < nblocks; ++n) step(n, std::true_type{}, std::true_type{});
+    step(nblocks, std::false_type{}, std::true_type{});
   }
 
   // ---- epilogue ----------------------------------------------------------------
