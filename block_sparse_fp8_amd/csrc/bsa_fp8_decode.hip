@@ -14,26 +14,31 @@
 // read and dequantised once.
 //
 // Per workgroup (sequence b, query token s, 16*NW heads), the list is walked
-// 32 tokens ("a block") at a time; every global load inside the loop is a
-// direct-to-LDS load, so each wait is an exact count of them:
-//   row ids: every wave copies the 32 entries of block n+5 into a ring of six
+// 32 tokens ("a block") at a time, one step per block with one barrier at its
+// end; every global load inside the loop is a direct-to-LDS load, so each wait
+// is an exact count of them.  Step n:
+//   row ids: every wave copies the 32 entries of block n+3 into a ring of six
 //      blocks in LDS (an entry is used only if it lies in the list and names a
 //      row: 0 <= entry < num_pages * page_size).
-//   staging: the rows of block n+3 go into a ring of three staging buffers
-//      (41 chunks of 16 bytes per row, 16 lanes per row).
-//   dequantise (block n+1, while block n is multiplied): E4M3 -> fp32, times
-//      the tile's descale, -> bfloat16 (round to nearest even) into one of two
-//      bfloat16 K tiles [32 tokens][576] in LDS, plus the 64 bfloat16 values.
-//   S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, wave w owning heads
+//   S^T = K . Q^T of block n on v_mfma_f32_16x16x32_bf16, wave w owning heads
 //      16w..16w+15; tokens sit in the K tile in the order those reads want, so
 //      each lane holds 8 consecutive tokens of one head, the layout of the P
-//      operand below.  Online softmax in the log2 domain with a lazily moved
-//      reference maximum; P rounded to bfloat16 into LDS.
-//   O^T += V^T . P^T: wave w owns 512/NW output dims for all heads, so each V
-//      value is read from LDS once per workgroup; V^T comes from the row-major
-//      K tile through the transposing read ds_read_b64_tr_b16.
-// Two barriers per block: before P.V (P ready) and after it (the next K tile
-// ready, the current one free).
+//      operand below.
+//   dequantise block n+1: E4M3 -> fp32, times the tile's descale, -> bfloat16
+//      (round to nearest even) into one of three bfloat16 K tiles [32
+//      tokens][576] in LDS, plus the 64 bfloat16 values; each wave converts
+//      its own tokens from its own staging region, and then refills that
+//      region with the rows of block n+2 (41 chunks of 16 bytes per row, 16
+//      lanes per row) without waiting for the other waves.
+//   O^T += V^T . P^T of block n-1: wave w owns 512/NW output dims for all
+//      heads, so each V value is read from LDS once per workgroup; V^T comes
+//      from the row-major K tile through the transposing read
+//      ds_read_b64_tr_b16.
+//   online softmax of block n in the log2 domain with a lazily moved reference
+//      maximum; P rounded to bfloat16 into one of two LDS buffers.
+// A K tile is rewritten two steps after its Q.K^T and one after its P.V, a P
+// buffer one step after its P.V, so the barrier at the end of each step orders
+// every reuse.
 // Epilogue: O = O_acc / l per head, bfloat16; LSE = ln sum exp(score).  A
 // query with no valid index gets O = 0 and LSE = -FLT_MAX.
 //
