@@ -302,12 +302,50 @@ bsa_fp8_prefill_kernel(Params p) {
   constexpr int kVBufs = QK8 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t v8_lds[kVBufs * kTile * kHeadDim];
   __shared__ __attribute__((aligned(16))) float ks_lds[kVBufs * kTile];
+  // FP8 paths: each lane's LDS read offsets, written once: the four K operand
+  // chunks of a block (two 16-byte chunks for each of the two 64-dim steps)
+  // and the four V operand columns of a 64-key step.  A step reads them back
+  // with two LDS loads instead of deriving them from the lane id again (which
+  // the loop cannot keep in registers).
+  __shared__ __attribute__((aligned(16))) int ofs_lds[QK8 ? kThreads * 8 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hd = lane >> 5;   // lane half
   const int col = lane & 31;  // query column owned by this lane within the wave
+
+  // LDS read offsets of lane ln within an E4M3 tile (FP8 paths: computed once
+  // and kept in ofs_lds; the f16 path derives the V offsets where it reads).
+  // K operand of the Q.K^T products: for the 64-dim step ks, the lane reads
+  // logical chunks 4ks + 2*(ln >> 5) and the next one of key row row0 (plus a
+  // per-block constant row offset, see kop).  Entry 2ks + h is chunk h.
+  auto k_offsets = [](int ln) -> v4i {
+    const int lcol = ln & 31;
+    const int row0 = ((lcol >> 2) & 1) * 32 + (((lcol >> 3) << 2) | (lcol & 3));
+    const int sw = swz8(row0);
+    const int c0 = 2 * (ln >> 5);
+    return v4i{row0 * kHeadDim + ((c0 ^ sw) << 4), row0 * kHeadDim + (((c0 + 1) ^ sw) << 4),
+               row0 * kHeadDim + (((c0 + 4) ^ sw) << 4), row0 * kHeadDim + (((c0 + 5) ^ sw) << 4)};
+  };
+  // V operand of the P.V products (transposing read): in each 16-lane group,
+  // source lane 2k+q addresses key row (half*32 + 8*rr + k) of a 64-key step
+  // at head-dim column 32d + 16*(group & 1) + 8q; result lane i then holds
+  // that column + i for those 8 keys.  The rows half*32 + 8*rr + k share the
+  // lane's chunk swizzle, so the offset for output block d serves every rr
+  // and both 64-key steps through constant offsets.
+  auto v_offset = [](int ln, int d) -> int {
+    const int grp = ln >> 4;
+    const int kk = (ln & 15) >> 1;
+    const int half = grp >> 1;
+    const int csw = (grp & 1) ^ kk ^ half;  // logical chunk 2d + (grp&1), swizzled
+    return (half * 32 + kk) * kHeadDim + 8 * (ln & 1) + (((2 * d) ^ csw) << 4);
+  };
+  if constexpr (QK8) {
+    *reinterpret_cast<v4i*>(&ofs_lds[tid * 8]) = k_offsets(lane);
+    *reinterpret_cast<v4i*>(&ofs_lds[tid * 8 + 4]) =
+        v4i{v_offset(lane, 0), v_offset(lane, 1), v_offset(lane, 2), v_offset(lane, 3)};
+  }
 
   // Work order.  The hardware hands consecutive workgroup ids to the 8 XCDs
   // round-robin.  Without a schedule, id i is remapped so that XCD (i % 8)
@@ -531,22 +569,22 @@ bsa_fp8_prefill_kernel(Params p) {
   constexpr int kPerBlock = QK8 ? 2 : 8;          // products per 32-key block
   constexpr int kAhead = QK8 ? 2 : 3;             // operand reads ahead of their product
   using KOp = std::conditional_t<QK8, v8i, v8h>;
-  auto kop = [&](int j, int ln, const uint8_t* kbuf) -> KOp {
+  // Lane ln's key row within block c is (c >> 1) * 64 + (c & 1) * 16 + row0,
+  // row0 = 32 * bit 2 of the query column + (bits 3, 1, 0 of it); the block's
+  // rows share row0's chunk swizzle (bits 0-2 and 5 of the row), so on the
+  // FP8 paths the block only adds a constant to the lane's four offsets `ko`
+  // (from k_offsets).
+  auto kop = [&](int j, int ln, const v4i& ko, const uint8_t* kbuf) -> KOp {
     const int c = j / kPerBlock, ks = j % kPerBlock;
-    const int lcol = ln & 31;
-    const int lhd = ln >> 5;
-    const int hi_a = (lcol >> 2) & 1;
-    const int ri_a = ((lcol >> 3) << 2) | (lcol & 3);
-    const int row = (c >> 1) * 64 + hi_a * 32 + (c & 1) * 16 + ri_a;
     if constexpr (QK8) {
-      const uint8_t* kp = kbuf + row * kHeadDim;
-      const int sw = swz8(row);
-      const int c0 = 4 * ks + 2 * lhd;  // logical chunks c0, c0+1: dims ks*64 + 32*lhd .. +31
-      const v4i lo = *reinterpret_cast<const v4i*>(kp + ((c0 ^ sw) << 4));
-      const v4i hi = *reinterpret_cast<const v4i*>(kp + (((c0 + 1) ^ sw) << 4));
+      const uint8_t* kp = kbuf + ((c >> 1) * 64 + (c & 1) * 16) * kHeadDim;
+      const v4i lo = *reinterpret_cast<const v4i*>(kp + ko[2 * ks]);
+      const v4i hi = *reinterpret_cast<const v4i*>(kp + ko[2 * ks + 1]);
       return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else {
-      return *reinterpret_cast<const v8h*>(kmat_lds + lhd * 2048 + row * 16 + ks * 4096);
+      const int lcol = ln & 31;
+      const int row = (c >> 1) * 64 + ((lcol >> 2) & 1) * 32 + (c & 1) * 16 + (((lcol >> 3) << 2) | (lcol & 3));
+      return *reinterpret_cast<const v8h*>(kmat_lds + (ln >> 5) * 2048 + row * 16 + ks * 4096);
     }
   };
   auto mfma_qk = [&](const KOp& a, int ks, const v16f& acc) -> v16f {
@@ -555,14 +593,14 @@ bsa_fp8_prefill_kernel(Params p) {
     else return mfma_f16(a, qh[ks], acc);
   };
   // All four blocks of a tile with no other work (the prologue).
-  auto qk_tile = [&](v16f* out, int ln, const uint8_t* kbuf) {
+  auto qk_tile = [&](v16f* out, int ln, const v4i& ko, const uint8_t* kbuf) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       v16f acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < kPerBlock; ++ks) acc = mfma_qk(kop(c * kPerBlock + ks, ln, kbuf), ks, acc);
+      for (int ks = 0; ks < kPerBlock; ++ks) acc = mfma_qk(kop(c * kPerBlock + ks, ln, ko, kbuf), ks, acc);
       out[c] = acc;
     }
   };
@@ -631,27 +669,21 @@ bsa_fp8_prefill_kernel(Params p) {
       const float e2 = __builtin_amdgcn_exp2f(fmaf(sb[r + 2], cscale, bias));
       const float e3 = __builtin_amdgcn_exp2f(fmaf(sb[r + 3], cscale, bias));
       ls += (e0 + e1) + (e2 + e3);
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+      // (the first pack's high half is replaced by the second: any old value
+      // serves, and on the FP8 paths e0's register, free by then, saves a
+      // zeroing move; the f16 path has no register to spare for it)
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, QK8 ? __float_as_int(e0) : 0, false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
       pk[c >> 1][(c & 1) * 4 + (r >> 2)] = w;
     }
     return ls;
   };
 
-  // O^T += V^T . P^T for 32 output dims (block d), both 64-key steps.
-  // Transposing read: in each 16-lane group, source lane 2k+q addresses key
-  // row (step*64 + half*32 + 8*rr + k) at head-dim column base + 8q; result
-  // lane i then holds column base + i for those 8 keys.  Rows sp*64 +
-  // half*32 + 8*rr + kk all share this lane's chunk swizzle, so one base per
-  // block serves the whole tile.
-  auto vread = [&](int x, int ln, int slot) -> v8i {  // x = sp*4 + d
-    const int grp = ln >> 4;
-    const int kk = (ln & 15) >> 1;
-    const int half = grp >> 1;
-    const int csw = (grp & 1) ^ kk ^ half;  // logical chunk 2d + (grp&1), swizzled
-    const uint8_t* vp = v8_lds + slot * kTile * kHeadDim + (half * 32 + kk) * kHeadDim + 8 * (ln & 1) +
-                        (((2 * (x & 3)) ^ csw) << 4) +
-                        (x >> 2) * 64 * kHeadDim;
+  // O^T += V^T . P^T for 32 output dims (block d), both 64-key steps; on the
+  // FP8 paths `vo` holds the lane's four v_offset values.
+  auto vread = [&](int x, int ln, const v4i& vo, int slot) -> v8i {  // x = sp*4 + d
+    const int vof = QK8 ? vo[x & 3] : v_offset(ln, x & 3);
+    const uint8_t* vp = v8_lds + slot * kTile * kHeadDim + vof + (x >> 2) * 64 * kHeadDim;
     v8i a;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -711,7 +743,7 @@ bsa_fp8_prefill_kernel(Params p) {
   v16f sa[4], sb[4];
   {
     widen_q();
-    qk_tile(sa, lane, kslot0);
+    qk_tile(sa, lane, QK8 ? k_offsets(lane) : v4i{}, kslot0);
     float tm = -INFINITY;
 #pragma unroll
     for (int c = 0; c < 4; ++c) tm = prep_block(sa[c], ks_read(c, lane, 0), c, n, lane, tm);
@@ -733,6 +765,8 @@ bsa_fp8_prefill_kernel(Params p) {
     constexpr int par = decltype(par_tag)::value;
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    int tl = tid;  // (opaque, like ln: the offsets are loaded, not derived)
+    if constexpr (QK8) asm volatile("" : "+v"(tl));
     // the next tile and its page ids first (a mask-chunk load inside the walk
     // is waited for at once, which must not also wait for the tile loads)
     const int n3 = n2 >= 0 ? walk.next(ln) : -1;
@@ -747,6 +781,7 @@ bsa_fp8_prefill_kernel(Params p) {
 
     // ---- A: exponentials of S(n), products of S(n1) ------------------------
     const uint8_t* k1 = QK8 ? kmat_lds + par * kTile * kHeadDim : kmat_lds;
+    const v4i ko = QK8 ? *reinterpret_cast<const v4i*>(&ofs_lds[tl * 8]) : v4i{};
     v8i pk[2];
     float ls = 0.0f;
     // Block by block, so that S(n) frees its registers as S(n1) needs them;
@@ -760,7 +795,7 @@ bsa_fp8_prefill_kernel(Params p) {
     constexpr int kRing = kAhead + 1;
     KOp ring[kRing];
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j) ring[j] = kop(j, ln, k1);
+    for (int j = 0; j < kAhead; ++j) ring[j] = kop(j, ln, ko, k1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       v16f acc;
@@ -769,7 +804,7 @@ bsa_fp8_prefill_kernel(Params p) {
 #pragma unroll
       for (int ks = 0; ks < kPerBlock; ++ks) {
         const int j = c * kPerBlock + ks;
-        if (j + kAhead < 4 * kPerBlock) ring[(j + kAhead) % kRing] = kop(j + kAhead, ln, k1);
+        if (j + kAhead < 4 * kPerBlock) ring[(j + kAhead) % kRing] = kop(j + kAhead, ln, ko, k1);
         acc = mfma_qk(ring[j % kRing], ks, acc);
       }
       nxt[c] = acc;
@@ -806,7 +841,8 @@ bsa_fp8_prefill_kernel(Params p) {
     // (the factor is exactly 1 when no row of the wave has a new maximum;
     // multiplying anyway keeps the phase free of branches)
     const float sc = rescale ? alpha : 1.0f;
-    v8i va0 = vread(0, ln, vs), va1 = vread(4, ln, vs);
+    const v4i vo = QK8 ? *reinterpret_cast<const v4i*>(&ofs_lds[tl * 8 + 4]) : v4i{};
+    v8i va0 = vread(0, ln, vo, vs), va1 = vread(4, ln, vo, vs);
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[0][r] *= sc;
     float tm = -INFINITY;
@@ -820,8 +856,8 @@ bsa_fp8_prefill_kernel(Params p) {
         tm = prep_block(nxt[d], kd, d, n1, ln, tm);
       }
       if (d < 3) {
-        va0 = vread(d + 1, ln, vs);
-        va1 = vread(5 + d, ln, vs);
+        va0 = vread(d + 1, ln, vo, vs);
+        va1 = vread(5 + d, ln, vo, vs);
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d + 1][r] *= sc;
       }
