@@ -512,9 +512,11 @@ def main():
                          "step that produces its inputs (GB/s against HBM); or FP8 sparse decode "
                          "(MQA over 656-byte cache rows, TFLOP/s against the bf16 matrix peak; "
                          "workload decode_b128 unless --workload names another decode config)")
-    ap.add_argument("--flushed", action="store_true",
-                    help="prefill only: also time the launches with a 512 MiB buffer written before "
-                         "each (cold caches); reported as kernel_ms_flushed_median")
+    ap.add_argument("--no-flushed", dest="flushed", action="store_false",
+                    help="prefill: skip the second timing pass, in which a 512 MiB buffer is written "
+                         "before each launch (cold caches; reported as kernel_ms_flushed_median)")
+    ap.add_argument("--flushed", dest="flushed", action="store_true",
+                    help="prefill: run the cold-cache pass (the default)")
     ap.add_argument("--graph", action="store_true",
                     help="decode only: capture the call in a HIP graph and time its replays")
     ap.add_argument("--splits", default="auto",
