@@ -106,6 +106,23 @@ def test_descales_not_powers_of_two(frac):
     compare(go2, gl2, eo, el, ea)
 
 
+@pytest.mark.parametrize("factor", [4.0, 16.0, 64.0])
+def test_peaked_softmax(factor):
+    """Q times a power of two (exact in bfloat16) spreads the scores over
+    tens to hundreds of binades: each head's softmax is dominated by a few
+    tokens, its reference maximum moves on many blocks (by more than 2^8 at a
+    time), and most P round to bfloat16 subnormals or zero.  The bound above
+    does not depend on the spread.  The split-list form is checked too."""
+    p = make_decode_problem("decode_tiny", seed=530, **SMALL[4])
+    p.q = (p.q * np.float32(factor)).astype(np.float32)
+    say(f"[gpu] decode peaked softmax, Q x{factor:g}")
+    go, gl = run_gpu(p)
+    eo, el, ea = D.sparse_decode(**p.oracle_kwargs(), with_abs=True)
+    say(f"[gpu]   ok {compare(go, gl, eo, el, ea)}")
+    go2, gl2 = run_gpu(p, num_splits=5)
+    say(f"[gpu]   split ok {compare(go2, gl2, eo, el, ea)}")
+
+
 def n_rows(p):
     return p.kv_cache.shape[0] * p.kv_cache.shape[1]
 
