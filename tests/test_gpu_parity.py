@@ -143,6 +143,23 @@ def test_zero_q_closed_form():
     np.testing.assert_allclose(go, eo, rtol=2 ** -7, atol=1e-4)
 
 
+@pytest.mark.parametrize("i", [0, 1])
+def test_descale_power_of_two_invariance(i):
+    """Q descales times 2^-7 with K descales times 2^7 leave every score
+    unchanged, and V descales times 8 scale O by 8: power-of-two factors are
+    exact in fp32 and bf16, so LSE must be bit-identical and O exactly 8x
+    (quant 0: per-tensor K descale; quant 1: per token and head)."""
+    p = make_problem("tiny", seed=19, **SMALL[i])
+    say(f"[gpu] descale power-of-two invariance, quant {p.quant_type}")
+    o1, l1 = run_gpu(p)
+    p.qscale = (p.qscale * np.float32(2.0 ** -7)).astype(np.float32)
+    p.kscale = (p.kscale * np.float32(2.0 ** 7)).astype(np.float32)
+    p.vscale = (p.vscale * np.float32(8.0)).astype(np.float32)
+    o2, l2 = run_gpu(p)
+    np.testing.assert_array_equal(l2, l1)
+    np.testing.assert_array_equal(o2, 8.0 * o1)
+
+
 def test_deterministic():
     p = make_problem("tiny", seed=18, **SMALL[4])
     say("[gpu] determinism")
