@@ -160,6 +160,28 @@ def test_descale_power_of_two_invariance(i):
     np.testing.assert_array_equal(o2, 8.0 * o1)
 
 
+def test_causal_equals_non_causal_below_the_diagonal():
+    """With every selected tile strictly below the diagonal (Lq = Lkv), no
+    selected key is past any query, so causal and non-causal runs visit the
+    same tiles in the same order with nothing to mask: bit-identical results
+    (and a mask that selects the diagonal tile must differ)."""
+    p = make_problem("tiny", seed=20, lq=(600, 256), lkv=(600, 256), hq=2, hkv=1, quant_type=1,
+                     kv_layout=0, page_size=64, keep=0.7)
+    bm = p.block_mask
+    mt, nt = bm.shape[2], bm.shape[3]
+    below = np.tril(np.ones((mt, nt), dtype=np.uint8), k=-1)
+    bm[:] = bm * below
+    say("[gpu] causal vs non-causal, tiles below the diagonal only")
+    oc, lc = run_gpu(p, causal=True)
+    on, ln = run_gpu(p, causal=False)
+    np.testing.assert_array_equal(oc, on)
+    np.testing.assert_array_equal(lc, ln)
+    bm[:, :, 1, 1] = 1  # the diagonal tile of Q tile 1: now the band mask matters
+    oc, lc = run_gpu(p, causal=True)
+    on, ln = run_gpu(p, causal=False)
+    assert not np.array_equal(lc, ln)
+
+
 def test_deterministic():
     p = make_problem("tiny", seed=18, **SMALL[4])
     say("[gpu] determinism")
