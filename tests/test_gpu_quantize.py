@@ -76,6 +76,29 @@ def test_quantize_append_bitwise(i, pow2):
     assert_same(got[:5], oracle_quantize(p, a, pow2))
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_power_of_two_input_scaling(pow2):
+    """Inputs times 2^5 (exact in bfloat16) leave every computed-descale code
+    unchanged and multiply those descales by 32 (amax/448 and its power-of-two
+    rounding both commute with the factor); all-zero rows keep descale 1.
+    Checked on Q and, with quant type 1, on the appended K slots and their
+    cached descales; the oracle is not involved."""
+    p = make_problem("tiny", seed=401, **CASES[1])  # quant type 1
+    a = append_inputs(p, seed=41)
+    say(f"[gpu] quantize power-of-two input scaling pow2={pow2}")
+    q1, qs1, kc1, _, ks1, _ = run_gpu_quantize(p, a, pow2)
+    a2 = dict(a, q=a["q"] * np.float32(32.0), k=a["k"] * np.float32(32.0))
+    q2, qs2, kc2, _, ks2, _ = run_gpu_quantize(p, a2, pow2)
+    np.testing.assert_array_equal(q2, q1)
+    zero_q = np.abs(a["q"]).max(axis=2) == 0
+    np.testing.assert_array_equal(qs2, np.where(zero_q, qs1, qs1 * np.float32(32.0)))
+    np.testing.assert_array_equal(kc2, kc1)
+    changed = ks1 != np.asarray(p.kscale, np.float32)  # the appended slots (old ones are kept)
+    assert changed.sum() > 0
+    ratio = ks2[changed] / ks1[changed]
+    assert np.all((ratio == np.float32(32.0)) | (ks1[changed] == np.float32(1.0)))
+
+
 def test_quantize_q_only_and_append_only():
     import block_sparse_fp8_amd as bsa
     p = make_problem("tiny", seed=420, **CASES[1])
