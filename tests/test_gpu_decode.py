@@ -127,6 +127,26 @@ def n_rows(p):
     return p.kv_cache.shape[0] * p.kv_cache.shape[1]
 
 
+def test_row_permutation_invariance():
+    """Moving every cache row to another place and renaming the list entries
+    to match (entries that name no row left as they are) gives bit-identical
+    results: an index is a cache row id and nothing else."""
+    p = make_decode_problem("decode_tiny", seed=531, **SMALL[2])
+    say("[gpu] decode row permutation")
+    o1, l1 = run_gpu(p)
+    rows = n_rows(p)
+    perm = np.random.default_rng(532).permutation(rows)
+    flat = p.kv_cache.reshape(rows, -1)
+    moved = np.empty_like(flat)
+    moved[perm] = flat
+    p.kv_cache = moved.reshape(p.kv_cache.shape)
+    valid = (p.indices >= 0) & (p.indices < rows)
+    p.indices = np.where(valid, perm[np.clip(p.indices, 0, rows - 1)], p.indices).astype(np.int32)
+    o2, l2 = run_gpu(p)
+    np.testing.assert_array_equal(o2, o1)
+    np.testing.assert_array_equal(l2, l1)
+
+
 def test_empty_lists_and_sequences():
     p = make_decode_problem("decode_tiny", seed=510, lkv=(300, 0, 90), s_q=2, h_q=64, topk=40)
     p.indices[0, 1, :] = -1                          # nothing selected
