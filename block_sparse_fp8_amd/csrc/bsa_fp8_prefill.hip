@@ -299,9 +299,12 @@ bsa_fp8_prefill_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t kst_lds[QK8 ? 16 : kTile * kHeadDim];
   // V and the K descales: on the FP8 paths two buffers each (step parity), so
   // that a step needs one barrier; the f16 path has room for one of each.
+  // After the descale buffers, one region of 1.0 (see the band tiles in the
+  // tile loop).
   constexpr int kVBufs = QK8 ? 2 : 1;
+  constexpr int kOnes = kVBufs;  // descale slot that holds 1.0 for every key
   __shared__ __attribute__((aligned(16))) uint8_t v8_lds[kVBufs * kTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) float ks_lds[kVBufs * kTile];
+  __shared__ __attribute__((aligned(16))) float ks_lds[(kVBufs + 1) * kTile];
   // FP8 paths: each lane's LDS read offsets, written once: the four K operand
   // chunks of a block (two 16-byte chunks for each of the two 64-dim steps)
   // and the four V operand columns of a 64-key step.  A step reads them back
@@ -341,6 +344,7 @@ bsa_fp8_prefill_kernel(Params p) {
     const int csw = (grp & 1) ^ kk ^ half;  // logical chunk 2d + (grp&1), swizzled
     return (half * 32 + kk) * kHeadDim + 8 * (ln & 1) + (((2 * d) ^ csw) << 4);
   };
+  if (tid < kTile) ks_lds[kOnes * kTile + tid] = 1.0f;
   if constexpr (QK8) {
     *reinterpret_cast<v4i*>(&ofs_lds[tid * 8]) = k_offsets(lane);
     *reinterpret_cast<v4i*>(&ofs_lds[tid * 8 + 4]) =
@@ -606,9 +610,8 @@ bsa_fp8_prefill_kernel(Params p) {
   };
 
   // ---- per-block softmax pieces ------------------------------------------------
-  // Scale + band mask + maximum of one block of S (in place); returns the
-  // block's partial maximum of the unscaled-by-cscale score.
-  // The K descales of block c (per-token K scales), read ahead of their use.
+  // The K descales of block c (per-token K scales), read ahead of their use;
+  // slot kOnes reads 1.0 for every key.
   auto ks_read = [&](int c, int ln, int slot) -> v16f {
     v16f k;
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
@@ -624,25 +627,41 @@ bsa_fp8_prefill_kernel(Params p) {
     }
     return k;
   };
-  auto prep_block = [&](v16f& sb, const v16f& kd, int c, int n, int ln, float run_max) -> float {
+  // Whether tile n reaches past a query of the wave (causal) or past the KV
+  // length, i.e. needs the band mask.
+  auto band_tile = [&](int n) -> bool {
+    return (p.causal && n * kTile + kTile - 1 > p_wave_min) || (n * kTile + kTile > lkv);
+  };
+  // Band mask of block c of tile n, in place.
+  auto mask_block = [&](v16f& sb, int c, int n, int ln) {
     const int lhd = ln >> 5;
     const int lcol = ln & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = n * kTile + (c >> 1) * 64 + lhd * 32 + (c & 1) * 16 + r;
+      const bool ok = j < lkv && (!p.causal || j <= p_wave_min + lcol);
+      sb[r] = ok ? sb[r] : -INFINITY;
+    }
+  };
+  // K descales of one block of S (in place).
+  auto scale_block = [&](v16f& sb, const v16f& kd) {
     if (QUANT == BSA_QUANT_Q_TOKHEAD_K_TOKHEAD_V_HEAD) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sb[r] *= kd[r];
     }
-    const bool band = (p.causal && n * kTile + kTile - 1 > p_wave_min) || (n * kTile + kTile > lkv);
-    if (band) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = n * kTile + (c >> 1) * 64 + lhd * 32 + (c & 1) * 16 + r;
-        const bool ok = j < lkv && (!p.causal || j <= p_wave_min + lcol);
-        sb[r] = ok ? sb[r] : -INFINITY;
-      }
-    }
+  };
+  // The block's partial maximum of the unscaled-by-cscale score, folded with
+  // run_max.
+  auto max_block = [&](const v16f& sb, float run_max) -> float {
     const float a = max3f(max3f(sb[0], sb[1], sb[2]), max3f(sb[3], sb[4], sb[5]), max3f(sb[6], sb[7], sb[8]));
     const float b2 = max3f(max3f(sb[9], sb[10], sb[11]), max3f(sb[12], sb[13], sb[14]), sb[15]);
     return max3f(a, b2, run_max);
+  };
+  // Scale + band mask + maximum of one block of S of tile n (in place).
+  auto prep_block = [&](v16f& sb, const v16f& kd, int c, int n, int ln, float run_max) -> float {
+    scale_block(sb, kd);
+    if (band_tile(n)) mask_block(sb, c, n, ln);
+    return max_block(sb, run_max);
   };
   // New running maximum from the four blocks' partial maxima (both lane
   // halves): sets alpha, bias and rescale.
@@ -846,14 +865,28 @@ bsa_fp8_prefill_kernel(Params p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[0][r] *= sc;
     float tm = -INFINITY;
+    // A band tile of S(n1) gets its descales and mask for all four blocks
+    // here, and the block loop below then scales it by the descale slot of
+    // 1.0: the loop has no branch, so the scheduler can move the next block's
+    // operand reads ahead of the current block's maximum.
+    const bool band1 = band_tile(n1);
+    if (band1) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        scale_block(nxt[d], ks_read(d, ln, vs));
+        mask_block(nxt[d], d, n1, ln);
+      }
+    }
+    const int kslot = band1 ? kOnes : vs;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       oacc[d] = mfma_f8(va0, pk[0], oacc[d]);
       oacc[d] = mfma_f8(va1, pk[1], oacc[d]);
       {
-        const v16f kd = ks_read(d, ln, vs);  // dead before the next block's V operands are read
+        const v16f kd = ks_read(d, ln, kslot);  // dead before the next block's V operands are read
         widen_k(d, ln);
-        tm = prep_block(nxt[d], kd, d, n1, ln, tm);
+        scale_block(nxt[d], kd);
+        tm = max_block(nxt[d], tm);
       }
       if (d < 3) {
         va0 = vread(d + 1, ln, vo, vs);
