@@ -571,7 +571,8 @@ bsa_fp8_prefill_kernel(Params p) {
   // operand of P.V needs.  Product j of a tile is block j / kPerBlock, k-step
   // j % kPerBlock; kop(j) reads its K operand.
   constexpr int kPerBlock = QK8 ? 2 : 8;          // products per 32-key block
-  constexpr int kAhead = QK8 ? 2 : 3;             // operand reads ahead of their product
+  // K operand reads ahead of their product (each split operand feeds two)
+  constexpr int kAhead = SPLIT ? 1 : (QK8 ? 2 : 3);
   using KOp = std::conditional_t<QK8, v8i, v8h>;
   // Lane ln's key row within block c is (c >> 1) * 64 + (c & 1) * 16 + row0,
   // row0 = 32 * bit 2 of the query column + (bits 3, 1, 0 of it); the block's
@@ -786,8 +787,19 @@ bsa_fp8_prefill_kernel(Params p) {
     asm volatile("" : "+v"(ln));
     int tl = tid;  // (opaque, like ln: the offsets are loaded, not derived)
     if constexpr (QK8) asm volatile("" : "+v"(tl));
-    // the next tile and its page ids first (a mask-chunk load inside the walk
-    // is waited for at once, which must not also wait for the tile loads)
+    // The first K operands of phase A (from the ring slot that already holds
+    // K(n1)) are read before anything else, so that their LDS round trip,
+    // and the offset table's before it, pass behind the tile walk and the
+    // loads below.  K operands are read kAhead products ahead, through the
+    // block boundaries.
+    const uint8_t* k1 = QK8 ? kmat_lds + par * kTile * kHeadDim : kmat_lds;
+    const v4i ko = QK8 ? *reinterpret_cast<const v4i*>(&ofs_lds[tl * 8]) : v4i{};
+    constexpr int kRing = kAhead + 1;
+    KOp ring[kRing];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) ring[j] = kop(j, ln, ko, k1);
+    // the next tile and its page ids (a mask-chunk load inside the walk is
+    // waited for at once, which must not also wait for the tile loads)
     const int n3 = n2 >= 0 ? walk.next(ln) : -1;
     const Pages pg_3 = n3 >= 0 ? lookup(n3, ln) : Pages{0};
     // loads of the step: V(n), the descales of n1, K(n2); on the FP8 paths V
@@ -799,8 +811,6 @@ bsa_fp8_prefill_kernel(Params p) {
     if (n2 >= 0) dma_tile(p.kc, n2, pg_2.kv, k2dst, ln);
 
     // ---- A: exponentials of S(n), products of S(n1) ------------------------
-    const uint8_t* k1 = QK8 ? kmat_lds + par * kTile * kHeadDim : kmat_lds;
-    const v4i ko = QK8 ? *reinterpret_cast<const v4i*>(&ofs_lds[tl * 8]) : v4i{};
     v8i pk[2];
     float ls = 0.0f;
     // Block by block, so that S(n) frees its registers as S(n1) needs them;
@@ -810,11 +820,6 @@ bsa_fp8_prefill_kernel(Params p) {
     // barrier).  The products run even after the last tile, on whatever the
     // K tile holds, and are not used: an assignment on one path only would
     // keep the old contents of `nxt` alive through the whole phase.
-    // K operands are read kAhead products ahead, through the block boundaries.
-    constexpr int kRing = kAhead + 1;
-    KOp ring[kRing];
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j) ring[j] = kop(j, ln, ko, k1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       v16f acc;
