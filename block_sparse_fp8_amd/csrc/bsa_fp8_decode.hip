@@ -290,19 +290,28 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
         pow2 = pow2 && (su & 0x807fffffu) == 0 && (su >> 23) >= 27 && (su >> 23) <= 227;
       }
       const bool all_pow2 = __builtin_amdgcn_ballot_w64(!(ok && !pow2)) == ~0ull;
+      // One branch around all four tiles (a branch per tile splits the
+      // scheduler's regions four times).
+      if (all_pow2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float scale = ok ? sc4[j] : 1.0f;
-        const v2i c2 = ok ? codes[j] : v2i{0, 0};
-        uint32_t w[4];
-        if (all_pow2) {
+        for (int j = 0; j < 4; ++j) {
+          const float scale = ok ? sc4[j] : 1.0f;
+          const v2i c2 = ok ? codes[j] : v2i{0, 0};
+          uint32_t w[4];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const uint32_t c = (uint32_t)c2[h];
             w[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false));
             w[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, true));
           }
-        } else {
+          *reinterpret_cast<v4i*>(dst + 256 * j + 16 * pp) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float scale = ok ? sc4[j] : 1.0f;
+          const v2i c2 = ok ? codes[j] : v2i{0, 0};
+          uint32_t w[4];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const uint32_t c = (uint32_t)c2[h];
@@ -311,8 +320,8 @@ __global__ void __launch_bounds__(NW * 64) bsa_fp8_decode_kernel(DecodeParams p)
             w[2 * h] = pack_bf16(lo[0] * scale, lo[1] * scale);
             w[2 * h + 1] = pack_bf16(hi[0] * scale, hi[1] * scale);
           }
+          *reinterpret_cast<v4i*>(dst + 256 * j + 16 * pp) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
         }
-        *reinterpret_cast<v4i*>(dst + 256 * j + 16 * pp) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       }
       if (pp >= 1 && pp <= 8)
         *reinterpret_cast<v4i*>(dst + 2 * kDimV + 16 * (pp - 1)) = ok ? rope : v4i{0, 0, 0, 0};
