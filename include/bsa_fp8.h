@@ -162,7 +162,10 @@ typedef struct {
  * cu_seqlens_q int32 [B+1], leading 0, non-decreasing, ends at T.
  * block_table  int32 [B, max_pages_per_seq]: logical page -> physical page.
  *              Only entries of pages that hold keys < Lkv_b are read.
- * seqlens_kv   int32 [B], Lkv_b.
+ * seqlens_kv   int32 [B], Lkv_b.  Query i of sequence b sits at position
+ *              Lkv_b - Lq_b + i (bottom-right alignment); Lq_b > Lkv_b is
+ *              allowed, and then, with the causal mask, the first
+ *              Lq_b - Lkv_b queries see no key (O = 0, LSE = -FLT_MAX).
  * block_mask   uint8 [B, Hq, mask_tiles_q, mask_tiles_kv], non-zero = compute
  *              that (Q tile, KV tile) pair.  NULL = every tile (dense path).
  *              Bits above the causal range, at or beyond Lkv_b, or on Q tiles

@@ -163,7 +163,7 @@ def make_problem(cfg, seed=None, fill="zero", lq=None, lkv=None, hq=None, hkv=No
         cfg = WorkloadConfig(**{**cfg.__dict__, **over})
     lq = np.asarray(cfg.lq, dtype=np.int64)
     lkv = np.asarray(cfg.lkv, dtype=np.int64)
-    assert lq.shape == lkv.shape and np.all(lq <= lkv)
+    assert lq.shape == lkv.shape
     B, Hq, Hkv, PS = len(lq), cfg.hq, cfg.hkv, cfg.page_size
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     T = int(lq.sum())
@@ -203,6 +203,8 @@ def make_problem(cfg, seed=None, fill="zero", lq=None, lkv=None, hq=None, hkv=No
             for m in range((int(lq[b]) + TILE - 1) // TILE):
                 p_min = int(lkv[b] - lq[b]) + m * TILE
                 p_max = int(lkv[b] - lq[b]) + min(m * TILE + TILE - 1, int(lq[b]) - 1)
+                if p_max < 0:  # more queries than keys: this Q tile sees no key
+                    continue
                 lo = max(0, p_min // TILE - cfg.window)
                 bm[b, :, m, lo:p_max // TILE + 1] = 1
     for (b, h, m) in cfg.zero_rows:

@@ -219,6 +219,16 @@ def test_sequences_without_queries():
     check(p, causal=False, label="sequences without queries, non-causal")
 
 
+def test_more_queries_than_keys():
+    """Lq > Lkv: query i sits at position Lkv - Lq + i, so (causal) the first Lq - Lkv
+    queries see no key, including whole waves inside a visited tile."""
+    p = make_problem("tiny", seed=72, lq=(300, 50), lkv=(100, 200), hq=4, hkv=2, quant_type=1,
+                     kv_layout=1, page_size=32, keep=0.6, fill="nan")
+    go, gl = check(p, label="more queries than keys")
+    assert np.all(go[:200] == 0.0) and np.all(gl[:, :200] == NEG_FLT_MAX)
+    check(p, causal=False, label="more queries than keys, non-causal")
+
+
 FULL = [("dense8k", 40, ()), ("sparse16k", 48, ()), ("varlen", 48, ((3, 5, 17), (0, 0, 0))),
         ("long128k", 64, ((0, 0, 0), (0, 31, 1023), (0, 7, 1)))]
 

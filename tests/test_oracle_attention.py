@@ -362,3 +362,28 @@ def test_bf16_rounding():
     x = np.array([1.0, 1.00390625, 1.005859375, 1.0 + 2 ** -7, -3.14159, 1e-30, 0.0])
     ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
     np.testing.assert_array_equal(A.round_bf16(x.astype(np.float32).astype(np.float64)), ref)
+
+
+def test_more_queries_than_keys():
+    """Bottom-right alignment with Lq > Lkv: query i sits at position Lkv - Lq + i, so
+    the first Lq - Lkv queries see no key (causal) and give O = 0, LSE = -FLT_MAX;
+    the rest follow brute force, as do the non-causal rows (empty only where the
+    block mask selects no tile)."""
+    p = make_problem("tiny", seed=71, lq=(300, 50), lkv=(100, 200), hq=4, hkv=2, quant_type=1,
+                     kv_layout=1, page_size=32, keep=0.6, fill="nan")
+    sizes = omega_sizes(p)
+    assert np.all(sizes[:, :200] == 0) and np.all(sizes[:, 200:300] > 0)
+    for causal in (True, False):
+        kw = {**p.oracle_kwargs(), "causal": causal}
+        ob, lb = A.brute_force(**kw)
+        for mode in ("exact", "emulate"):
+            o, l = A.prefill(**kw, mode=mode)
+            if mode == "exact":
+                np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+            if causal:
+                assert np.all(o[:200] == 0.0) and np.all(l[:, :200] == NEG_FLT_MAX)
+                assert np.all(l[:, 200:] > NEG_FLT_MAX)
+            empty = l == NEG_FLT_MAX
+            assert np.array_equal(empty, lb == NEG_FLT_MAX)
+            assert np.all(o.transpose(1, 0, 2)[empty] == 0.0)
