@@ -178,7 +178,7 @@ typedef struct {
  * stream       hipStream_t to enqueue on.
  *
  * Preconditions the library cannot check (caller's contract):
- *   Lq_b <= Lkv_b; max_seqlen_q >= every Lq_b; with a mask,
+ *   max_seqlen_q >= every Lq_b; with a mask,
  *   Lkv_b <= 128 * mask_tiles_kv (tiles beyond the mask width count as off);
  *   block_table entries of pages holding keys < Lkv_b are valid page ids;
  *   every descale is finite and >= 0.
@@ -314,9 +314,10 @@ int bsa_fp8_schedule(const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
  *              max_pages_per_seq, kv_layout are read; the other fields must be
  *              valid as for bsa_fp8_prefill (their values are not used).
  * Every array is a device pointer owned by the caller; one kernel is enqueued
- * on `stream`.  Preconditions as for bsa_fp8_prefill (Lq_b <= Lkv_b, valid
- * block-table entries for the appended positions, finite inputs, positive
- * given descales).  Errors: as for bsa_fp8_prefill, plus BSA_ERR_SCALE_MODE;
+ * on `stream`.  Preconditions: Lq_b <= Lkv_b (every appended position is at
+ * least 0; the prefill itself also accepts Lq_b > Lkv_b), valid block-table
+ * entries for the appended positions, finite inputs, positive given
+ * descales.  Errors: as for bsa_fp8_prefill, plus BSA_ERR_SCALE_MODE;
  * BSA_ERR_NULL_POINTER when a pointer the requested parts need is NULL or
  * only one of k_in / v_in is given.
  */

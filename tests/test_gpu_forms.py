@@ -24,6 +24,8 @@ SMALL = [
     dict(lq=(64, 256, 1), lkv=(250, 256, 700), hq=4, hkv=1, quant_type=0, kv_layout=1, page_size=64,
          keep=0.7),
     dict(lq=(1000,), lkv=(1500,), hq=16, hkv=1, quant_type=1, kv_layout=0, page_size=64, keep=0.4),
+    dict(lq=(300, 50), lkv=(100, 200), hq=4, hkv=2, quant_type=1, kv_layout=1, page_size=32,
+         keep=0.6),  # more queries than keys: the first 200 rows see no key
 ]
 
 
