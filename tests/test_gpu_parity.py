@@ -6,6 +6,7 @@ launch is the full problem, exactly as the benchmark times it), plus
 properties that hold for every output element.
 """
 import numpy as np
+import torch
 import pytest
 
 from oracle import attention as A
@@ -218,6 +219,53 @@ def test_sequences_without_queries():
     check(p, label="sequences without queries")
     check(p, causal=False, label="sequences without queries, non-causal")
 
+
+def test_lse_not_requested_leaves_output_unchanged():
+    """lse = NULL: the epilogue skips the LSE store; O is the same bit for bit."""
+    import block_sparse_fp8_amd as bsa
+    p = make_problem("tiny", seed=81, **SMALL[1])
+    say("[gpu] prefill without lse")
+    d = p.to_device("cuda")
+    args = (d["q"], d["kcache"], d["vcache"], d["qscale"], d["kscale"], d["vscale"], d["cu_seqlens_q"],
+            d["block_table"], d["seqlens_kv"], d["block_mask"], p.quant_type, p.page_size)
+    kw = dict(max_seqlen_q=p.max_seqlen_q, kv_layout=p.kv_layout, causal=p.causal,
+              softmax_scale=p.softmax_scale)
+    o1, l1 = bsa.bsa_fp8_prefill(*args, **kw)
+    o2, l2 = bsa.bsa_fp8_prefill(*args, **kw, return_lse=False)
+    assert l2 is None
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_zero_softmax_scale_is_the_mean_of_the_selected_values():
+    """softmax_scale = 0: every selected key weighs the same, P' = 256 is exact in E4M3, so
+    O is the mean of the dequantised V rows of each query's keys and LSE = log(count).
+    The closed form is computed here from the codes (torch's E4M3 decoding), not by the oracle."""
+    p = make_problem("tiny", seed=82, **SMALL[1])
+    p.softmax_scale = 0.0
+    go, gl = check(p, label="softmax scale 0")
+    T, Hq, _ = p.q.shape
+    Hkv = p.vcache.shape[1] if p.kv_layout == 1 else p.vcache.shape[2]
+    codes = torch.from_numpy(np.ascontiguousarray(p.vcache)).view(torch.float8_e4m3fn).double().numpy()
+    vs = np.asarray(p.vscale, dtype=np.float64)
+    for b in range(len(p.seqlens_kv)):
+        t0, t1 = int(p.cu_seqlens_q[b]), int(p.cu_seqlens_q[b + 1])
+        lq, lkv = t1 - t0, int(p.seqlens_kv[b])
+        j = np.arange(lkv)
+        page, slot = p.block_table[b, j // p.page_size], j % p.page_size
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            v = (codes[page, g, slot] if p.kv_layout == 1 else codes[page, slot, g])
+            v = v * (vs[g] if vs.size > 1 else vs[0])                     # [lkv, 128]
+            for t in range(lq):
+                on = (p.block_mask[b, h, t // 128, j // 128] != 0) & (j <= lkv - lq + t)
+                n = int(on.sum())
+                if n == 0:
+                    assert np.all(go[t0 + t, h] == 0.0) and gl[h, t0 + t] == NEG_FLT_MAX
+                    continue
+                mean = v[on].mean(axis=0)
+                tol = 2.0 ** -8 * np.abs(mean) + 2.0 ** -12 * np.abs(v[on]).max()
+                assert np.all(np.abs(go[t0 + t, h] - mean) <= tol), (b, h, t)
+                assert abs(gl[h, t0 + t] - np.log(n)) <= 1e-5 * max(1.0, np.log(n)), (b, h, t)
 
 def test_more_queries_than_keys():
     """Lq > Lkv: query i sits at position Lkv - Lq + i, so (causal) the first Lq - Lkv
