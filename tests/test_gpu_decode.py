@@ -106,6 +106,35 @@ def test_descales_not_powers_of_two(frac):
     compare(go2, gl2, eo, el, ea)
 
 
+def test_zero_softmax_scale_is_the_mean_of_the_selected_rows():
+    """softmax_scale = 0: every valid entry weighs 1 (P = 2^0 is exact in bfloat16), so O
+    is the mean of the named rows' dequantised values (a repeated entry counts twice) and
+    LSE = log(count).  The closed form decodes the row bytes with torch's E4M3 type, not
+    with the oracle."""
+    import torch
+    from parity_util import NEG_FLT_MAX
+    p = make_decode_problem("decode_tiny", seed=530, **SMALL[2])
+    p.softmax_scale = 0.0
+    say("[gpu] decode softmax scale 0, plain and 3 parts")
+    got = [run_gpu(p), run_gpu(p, num_splits=3)]
+    rows = p.kv_cache.reshape(-1, p.kv_cache.shape[-1])
+    codes = torch.from_numpy(np.ascontiguousarray(rows[:, :512])).view(torch.float8_e4m3fn).double().numpy()
+    B, s_q, h_q, _ = p.q.shape
+    for b in range(B):
+        for s in range(s_q):
+            idx = p.indices[b, s].astype(np.int64)
+            idx = idx[(idx >= 0) & (idx < rows.shape[0])]
+            for go, gl in got:
+                if idx.size == 0:
+                    assert np.all(go[b, s] == 0.0) and np.all(gl[b, :, s] == NEG_FLT_MAX)
+                    continue
+                scales = np.ascontiguousarray(rows[idx, 512:528]).view(np.float32).astype(np.float64)
+                v = codes[idx] * np.repeat(scales, 128, axis=1)               # [n, 512]
+                mean = v.mean(axis=0)
+                tol = 2.0 ** -8 * np.abs(mean) + 2.0 ** -14 * np.abs(v).max()
+                assert np.all(np.abs(go[b, s] - mean[None, :]) <= tol[None, :]), (b, s)
+                np.testing.assert_allclose(gl[b, :, s], np.log(idx.size), rtol=1e-5, atol=1e-6)
+
 @pytest.mark.parametrize("factor", [4.0, 16.0, 64.0])
 def test_peaked_softmax(factor):
     """Q times a power of two (exact in bfloat16) spreads the scores over
