@@ -524,6 +524,8 @@ def main():
                          "choice; 1 is the single-pass kernel)")
     ap.add_argument("--qk", choices=tuple(QK_CODES), default="default",
                     help="matrix path of the prefill's Q.K^T products (bsa_qk_precision)")
+    ap.add_argument("--q-layout", choices=("tnd", "ntd"), default="tnd",
+                    help="prefill: query layout, TND (q [T,Hq,128]) or NTD (q [Hq,T,128], qscale [Hq,T])")
     ap.add_argument("--schedule", action="store_true",
                     help="run the scheduling pre-pass inside every step and launch the prefill "
                          "in its task order")
@@ -583,6 +585,12 @@ def main():
         si = torch.from_numpy(idx).cuda()
         sl = torch.from_numpy(slen).cuda()
     mask = d["block_mask"] if si is None else None
+    q_dev, qs_dev, q_layout = d["q"], d["qscale"], bsa.QLayout.TND
+    if args.q_layout == "ntd":
+        from synth import to_ntd
+        q_ntd, qs_ntd = to_ntd(p)
+        q_dev, qs_dev = torch.from_numpy(q_ntd).cuda(), torch.from_numpy(qs_ntd).cuda()
+        q_layout = bsa.QLayout.NTD
     sched = ws = None
     if args.schedule:
         ntasks = len(p.seqlens_kv) * Hq * ((p.max_seqlen_q + TILE - 1) // TILE)
@@ -598,7 +606,7 @@ def main():
     qk = QK_CODES[args.qk]
 
     def step():
-        if args.form == "mask" and not args.schedule and qk == 0:
+        if args.form == "mask" and not args.schedule and qk == 0 and args.q_layout == "tnd":
             bsa.bsa_fp8_prefill(d["q"], d["kcache"], d["vcache"], d["qscale"], d["kscale"],
                                 d["vscale"], d["cu_seqlens_q"], d["block_table"], d["seqlens_kv"],
                                 d["block_mask"], p.quant_type, p.page_size,
@@ -607,11 +615,11 @@ def main():
             return
         if args.schedule:
             pre_pass()
-        bsa.bsa_fp8_prefill_ex(d["q"], d["kcache"], d["vcache"], d["qscale"], d["kscale"],
+        bsa.bsa_fp8_prefill_ex(q_dev, d["kcache"], d["vcache"], qs_dev, d["kscale"],
                                d["vscale"], d["cu_seqlens_q"], d["block_table"], d["seqlens_kv"],
                                mask, p.quant_type, p.page_size, max_seqlen_q=p.max_seqlen_q,
                                kv_layout=p.kv_layout, causal=p.causal,
-                               softmax_scale=p.softmax_scale, sparse_indices=si,
+                               softmax_scale=p.softmax_scale, q_layout=q_layout, sparse_indices=si,
                                sparse_seq_len=sl, schedule=sched, qk_precision=qk, out=out, lse=lse)
 
     warmup = warm_up(step, args)
@@ -653,7 +661,8 @@ def main():
         del flush
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
     # the traffic record is taken on the default launch (mask form, default Q.K^T path)
-    recorded = args.form == "mask" and not args.schedule and qk_path(args.qk) == DEFAULT_QK
+    recorded = (args.form == "mask" and not args.schedule and qk_path(args.qk) == DEFAULT_QK
+                and args.q_layout == "tnd")
     rec = traffic_record(p.cfg.name) if recorded else None
     dram_read_gbps = None
     if rec is not None:
@@ -663,7 +672,8 @@ def main():
     kv_bytes = n_act * (KV_BYTES_PER_TILE + (TILE * 4 if p.quant_type == 1 else 0))
     tflops = flop / (wall / args.steps) / 1e12
     achieved = flop / avg_kernel_s / 1e12
-    crec = clock_record(p.cfg.name, args.qk) if args.form == "mask" and not args.schedule else None
+    crec = (clock_record(p.cfg.name, args.qk)
+            if args.form == "mask" and not args.schedule and args.q_layout == "tnd" else None)
     clk = None if crec is None else crec["clock_ghz_mean"]
     res = {
         "metric": METRIC,
@@ -679,7 +689,7 @@ def main():
         "dtype": QK_DTYPES[qk_path(args.qk)],
         "data": "synthetic (seeded N(0,1) quantised to E4M3, random paging and block mask)",
         "config": {"workload": f"{p.cfg.name}: {p.cfg.description}", "active_tiles": n_act,
-                   "q_tokens": T, "causal": bool(p.causal), "sparsity_form": args.form,
+                   "q_tokens": T, "causal": bool(p.causal), "sparsity_form": args.form, "q_layout": args.q_layout,
                    "schedule_pre_pass": bool(args.schedule), "qk_precision": args.qk},
         "tokens_per_s": round(T / (wall / args.steps), 1),
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
