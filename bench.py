@@ -308,7 +308,8 @@ def bench_quantize_append(p, args):
                                     d["block_table"], ks, vs, p.quant_type, p.page_size,
                                     kcache=d["kcache"], vcache=d["vcache"],
                                     kscale_cache=kcache_scale, kv_layout=p.kv_layout,
-                                    q_out=q_out, qscale_out=qs_out)
+                                    q_out=q_out, qscale_out=qs_out,
+                                    scale_mode=1 if args.scale_mode == "pow2" else 0)
 
     warmup = warm_up(step, args)
     stream = torch.cuda.current_stream()
@@ -337,12 +338,13 @@ def bench_quantize_append(p, args):
         "data": "synthetic (seeded N(0,1) bfloat16)",
         "config": {"workload": f"{p.cfg.name} query chunk: {T} tokens, Hq {Hq}, Hkv {Hkv}, "
                                f"quant {p.quant_type}", "rows": rows_q + 2 * rows_kv,
-                   "bytes_per_launch": nbytes},
+                   "bytes_per_launch": nbytes, "scale_mode": args.scale_mode},
         "kernel_ms_min": round(float(kernel_ms.min()), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": {"bound": "hbm", "achieved": round(nbytes / med / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(nbytes / med / 1e9 / PEAK_HBM_GBPS, 4),
-                     "traffic": recorded_traffic(p.cfg.name, "quantize_append")},
+                     "traffic": (recorded_traffic(p.cfg.name, "quantize_append")
+                                 if args.scale_mode == "amax" else None)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_quantize(p, a, args.cpu_budget)
@@ -524,6 +526,8 @@ def main():
                          "choice; 1 is the single-pass kernel)")
     ap.add_argument("--qk", choices=tuple(QK_CODES), default="default",
                     help="matrix path of the prefill's Q.K^T products (bsa_qk_precision)")
+    ap.add_argument("--scale-mode", choices=("amax", "pow2"), default="amax",
+                    help="quantize_append: descales amax/448 as computed, or rounded up to powers of two")
     ap.add_argument("--q-layout", choices=("tnd", "ntd"), default="tnd",
                     help="prefill: query layout, TND (q [T,Hq,128]) or NTD (q [Hq,T,128], qscale [Hq,T])")
     ap.add_argument("--schedule", action="store_true",
